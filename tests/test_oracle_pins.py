@@ -1,0 +1,10 @@
+"""The fp64 oracle against its pins (closed forms, invariants, library special cases, brute force)."""
+import pytest
+
+import oracle
+from tests import oracle_pins
+
+
+@pytest.mark.parametrize("pin", oracle_pins.ALL_PINS, ids=lambda f: f.__name__)
+def test_pin(pin):
+    pin(oracle)
