@@ -1,0 +1,123 @@
+// HBM-bound helpers: the standalone log-sum-exp combine of two normalised
+// partial results, and the backward's D = rowsum(dO * O).
+#include "ra_internal.h"
+
+namespace ra {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+// Weights of the combine (o, lse) = (o_a, lse_a) (+) (o_b, lse_b).
+__device__ inline void combine_weights(float la, float lb, float& lse, float& wa, float& wb) {
+  const float mx = fmaxf(la, lb);
+  if (mx == -INFINITY) {
+    lse = -INFINITY; wa = 0.f; wb = 0.f;
+    return;
+  }
+  const float ea = __expf(la - mx), eb = __expf(lb - mx);   // exp(-inf) = 0
+  const float s = ea + eb;
+  lse = mx + __logf(s);
+  const float inv = 1.f / s;
+  wa = ea * inv;
+  wb = eb * inv;
+}
+
+// A group of 32 lanes owns one row (so the in-place lse_b update cannot race
+// with another row's reads); each lane handles D/32 consecutive floats.
+template <int D>
+__global__ __launch_bounds__(256) void merge_kernel(int rows, const float* __restrict__ o_a,
+                                                    const float* __restrict__ lse_a, float* o_b,
+                                                    float* lse_b, void* out, Strides os, int hq, int sq,
+                                                    int dtype) {
+  constexpr int PER = D / 32;   // 4 (D=128) or 2 (D=64)
+  const int lane = threadIdx.x & 31;
+  const int group = (blockIdx.x * blockDim.x + threadIdx.x) >> 5;
+  const int groups = (gridDim.x * blockDim.x) >> 5;
+  for (int row = group; row < rows; row += groups) {
+    const float la = lse_a[row], lb = lse_b[row];
+    float lse, wa, wb;
+    combine_weights(la, lb, lse, wa, wb);
+    const size_t base = (size_t)row * D + lane * PER;
+    float r[PER];
+    if constexpr (PER == 4) {
+      const f32x4 a = *(const f32x4*)(o_a + base);
+      const f32x4 b = *(const f32x4*)(o_b + base);
+      for (int e = 0; e < 4; ++e) r[e] = wa * a[e] + wb * b[e];
+      *(f32x4*)(o_b + base) = f32x4{r[0], r[1], r[2], r[3]};
+    } else {
+      for (int e = 0; e < PER; ++e) r[e] = wa * o_a[base + e] + wb * o_b[base + e];
+      for (int e = 0; e < PER; ++e) o_b[base + e] = r[e];
+    }
+    if (out) {
+      const int b = row / (hq * sq), h = (row / sq) % hq, s = row % sq;
+      const size_t ob = b * os.b + h * os.h + s * os.s + lane * PER;
+      if (dtype == BF16) {
+        for (int e = 0; e < PER; ++e) ((__bf16*)out)[ob + e] = (__bf16)r[e];
+      } else {
+        for (int e = 0; e < PER; ++e) ((float*)out)[ob + e] = r[e];
+      }
+    }
+    if (lane == 0) lse_b[row] = lse;
+  }
+}
+
+hipError_t launch_merge(int rows, int d, const float* o_a, const float* lse_a, float* o_b, float* lse_b,
+                        void* out, Strides os, int hq, int sq, int dtype, hipStream_t st) {
+  if (rows == 0) return hipSuccess;
+  long blocks = ((long)rows * 32 + 255) / 256;
+  if (blocks > 8192) blocks = 8192;
+  if (d == 128)
+    merge_kernel<128><<<(unsigned)blocks, 256, 0, st>>>(rows, o_a, lse_a, o_b, lse_b, out, os, hq, sq, dtype);
+  else
+    merge_kernel<64><<<(unsigned)blocks, 256, 0, st>>>(rows, o_a, lse_a, o_b, lse_b, out, os, hq, sq, dtype);
+  return hipGetLastError();
+}
+
+// delta[row] = sum_d dO[row, d] * O[row, d]; D/8 lanes per row, 8 elements per lane.
+template <int D, typename T>
+__global__ __launch_bounds__(256) void bwd_pre_kernel(int B, int hq, int sq, const T* __restrict__ out,
+                                                      const T* __restrict__ d_o, Strides qs,
+                                                      float* __restrict__ delta) {
+  constexpr int G = D / 8;   // lanes per row (16 or 8)
+  const long rows = (long)B * hq * sq;
+  const int sub = threadIdx.x % G;
+  long row = ((long)blockIdx.x * blockDim.x + threadIdx.x) / G;
+  const long stride_rows = ((long)gridDim.x * blockDim.x) / G;
+  for (; row < rows; row += stride_rows) {   // uniform trip count per G-lane group
+    const int b = row / ((long)hq * sq), h = (row / sq) % hq, s = row % sq;
+    const size_t off = b * qs.b + h * qs.h + s * qs.s + sub * 8;
+    float acc = 0.f;
+    if constexpr (sizeof(T) == 2) {
+      const bf16x8 x = *(const bf16x8*)(out + off);
+      const bf16x8 y = *(const bf16x8*)(d_o + off);
+      for (int e = 0; e < 8; ++e) acc += (float)x[e] * (float)y[e];
+    } else {
+      const f32x4 x0 = *(const f32x4*)(out + off), x1 = *(const f32x4*)(out + off + 4);
+      const f32x4 y0 = *(const f32x4*)(d_o + off), y1 = *(const f32x4*)(d_o + off + 4);
+      for (int e = 0; e < 4; ++e) acc += x0[e] * y0[e] + x1[e] * y1[e];
+    }
+#pragma unroll
+    for (int o = G / 2; o >= 1; o >>= 1) acc += __shfl_xor(acc, o, G);
+    if (sub == 0) delta[row] = acc;
+  }
+}
+
+hipError_t launch_bwd_preprocess(int B, int hq, int sq, int d, const void* out, const void* d_o,
+                                 Strides qs, int dtype, float* delta, hipStream_t st) {
+  const long rows = (long)B * hq * sq;
+  if (rows == 0) return hipSuccess;
+  const int G = d / 8;
+  long blocks = (rows * G + 255) / 256;
+  if (blocks > 16384) blocks = 16384;
+  if (dtype == BF16) {
+    if (d == 128) bwd_pre_kernel<128, __bf16><<<(unsigned)blocks, 256, 0, st>>>(B, hq, sq, (const __bf16*)out, (const __bf16*)d_o, qs, delta);
+    else bwd_pre_kernel<64, __bf16><<<(unsigned)blocks, 256, 0, st>>>(B, hq, sq, (const __bf16*)out, (const __bf16*)d_o, qs, delta);
+  } else {
+    if (d == 128) bwd_pre_kernel<128, float><<<(unsigned)blocks, 256, 0, st>>>(B, hq, sq, (const float*)out, (const float*)d_o, qs, delta);
+    else bwd_pre_kernel<64, float><<<(unsigned)blocks, 256, 0, st>>>(B, hq, sq, (const float*)out, (const float*)d_o, qs, delta);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace ra

@@ -1,0 +1,108 @@
+// Internal declarations shared by the host driver and the HIP kernels of
+// libringattn.  Not part of the public C ABI (include/ringattn.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ra {
+
+// Positions/documents are summarised per run of TILE tokens; the step
+// kernels' key tile is this many tokens and query tiles are multiples of it.
+constexpr int TILE = 64;
+constexpr int POS_INVALID = 0x7fffffff;   // sentinel: a key slot past the end of the block
+
+enum Mask { MASK_NONE = 0, MASK_CAUSAL = 1, MASK_DOC_CAUSAL = 2 };
+enum DType { F32 = 0, BF16 = 1 };
+enum StepFlags { FLAG_FIRST = 1, FLAG_LAST = 2, FLAG_NO_SKIP = 4 };
+
+// Per-tile summary: {min pos, max pos, min doc, max doc} over the tile's tokens.
+struct TileRange {
+  int min_pos, max_pos, min_doc, max_doc;
+};
+
+__host__ __device__ inline int n_tiles(int s) { return (s + TILE - 1) / TILE; }
+
+struct Strides {
+  int64_t b, h, s;
+};
+
+struct FwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  float* o_acc;       // dense [B][Hq][Sq][D]
+  float* lse;         // dense [B][Hq][Sq]
+  void* out;          // q strides, problem dtype; written when FLAG_LAST and non-null
+  const int* q_pos;
+  const int* kv_pos;
+  const int* q_doc;
+  const int* kv_doc;
+  const TileRange* q_tiles;
+  const TileRange* kv_tiles;
+  Strides qs, kvs;
+  int B, hq, hkv, sq, sk;
+  float scale;        // softmax scale
+  float scale_log2;   // softmax scale * log2(e)
+  int mask;
+  int flags;
+};
+
+struct BwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* d_o;    // q strides
+  const float* lse;   // dense [B][Hq][Sq]
+  const float* delta; // dense [B][Hq][Sq]
+  float* dq;          // dense [B][Hq][Sq][D]
+  float* dk;          // dense [B][Hkv][Sk][D]
+  float* dv;
+  const int* q_pos;
+  const int* kv_pos;
+  const int* q_doc;
+  const int* kv_doc;
+  const TileRange* q_tiles;
+  const TileRange* kv_tiles;
+  Strides qs, kvs;
+  int B, hq, hkv, sq, sk;
+  float scale;
+  float scale_log2;
+  int mask;
+  int flags;
+};
+
+// Tile classes of a (query tile, key tile) pair.
+enum TileClass { TILE_EMPTY = 0, TILE_FULL = 1, TILE_PARTIAL = 2 };
+
+// Classify a query-range/key-tile pair.  `kv_complete` says all TILE key slots
+// of the tile hold real keys.
+__host__ __device__ inline int classify(const TileRange& qr, const TileRange& kr, bool kv_complete,
+                                        int mask) {
+  if (mask != MASK_NONE) {
+    if (kr.min_pos > qr.max_pos) return TILE_EMPTY;
+    if (mask == MASK_DOC_CAUSAL && (kr.max_doc < qr.min_doc || kr.min_doc > qr.max_doc)) return TILE_EMPTY;
+  }
+  if (!kv_complete) return TILE_PARTIAL;
+  if (mask == MASK_NONE) return TILE_FULL;
+  if (kr.max_pos > qr.min_pos) return TILE_PARTIAL;
+  if (mask == MASK_DOC_CAUSAL &&
+      !(kr.min_doc == kr.max_doc && qr.min_doc == qr.max_doc && kr.min_doc == qr.min_doc))
+    return TILE_PARTIAL;
+  return TILE_FULL;
+}
+
+// ---- launchers (each returns hipGetLastError() of its launches) ----
+hipError_t launch_tile_ranges(const int* pos, const int* doc, int n, TileRange* out, hipStream_t st);
+hipError_t launch_docs_from_cu(const int* cu, int n_docs, int first, int n, int* doc, hipStream_t st);
+hipError_t launch_merge(int rows, int d, const float* o_a, const float* lse_a, float* o_b, float* lse_b,
+                        void* out, Strides os, int hq, int sq, int dtype, hipStream_t st);
+hipError_t launch_bwd_preprocess(int B, int hq, int sq, int d, const void* out, const void* d_o,
+                                 Strides qs, int dtype, float* delta, hipStream_t st);
+hipError_t launch_fill_nan(void* p, size_t bytes, hipStream_t st);
+hipError_t launch_fwd_bf16(const FwdArgs& a, int d, hipStream_t st);
+hipError_t launch_fwd_f32(const FwdArgs& a, int d, hipStream_t st);
+hipError_t launch_bwd_bf16(const BwdArgs& a, int d, hipStream_t st);
+hipError_t launch_bwd_f32(const BwdArgs& a, int d, hipStream_t st);
+
+}  // namespace ra

@@ -1,0 +1,168 @@
+"""The C ABI on the host: the library loads, exports what include/ringattn.h declares,
+and its pure-host validation rejects bad arguments with the documented status and
+without touching any output.  No kernel is launched here (no GPU needed)."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from ring_attention_ringattn_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ringattn.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(ringattn_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_exports_match_library():
+    names = declared_functions()
+    assert len(names) == 10, names
+    assert sorted(_lib.EXPORTS) == names
+    lib = _lib.load()
+    for n in names:
+        assert hasattr(lib, n), n
+    assert lib.ringattn_version() == 1
+
+
+def _problem(**kw):
+    """A valid bf16 problem; dense strides follow the sizes unless given."""
+    p = _lib.RaProblem()
+    p.batch, p.hq, p.hkv, p.head_dim, p.sq, p.sk = 1, 4, 2, 128, 256, 256
+    p.dtype, p.softmax_scale = _lib.RA_BF16, 0.0
+    for k, v in kw.items():
+        if k not in ("q_stride", "kv_stride"):
+            setattr(p, k, v)
+    sq, sk, d = max(p.sq, 1), max(p.sk, 1), p.head_dim
+    p.q_stride[:] = kw.get("q_stride", (p.hq * sq * d, sq * d, d))
+    p.kv_stride[:] = kw.get("kv_stride", (p.hkv * sk * d, sk * d, d))
+    return p
+
+
+class Host:
+    """Host buffers standing in for device pointers: validation must reject before touching them."""
+
+    def __init__(self):
+        self.bufs = {n: np.full(64, 7.0, dtype=np.float32) for n in
+                     ("q", "k", "v", "o", "lse", "out", "qp", "kp", "qd", "kd", "ws", "do", "delta", "dq", "dk", "dv")}
+
+    def p(self, n, off=0):
+        return ctypes.c_void_p(self.bufs[n].ctypes.data + off)
+
+    def untouched(self):
+        return all(np.all(b == 7.0) for b in self.bufs.values())
+
+
+def step_fwd(h, p, mask=1, flags=0, ws_bytes=1 << 20, **ptr):
+    args = dict(q=h.p("q"), k=h.p("k"), v=h.p("v"), o=h.p("o"), lse=h.p("lse"), out=h.p("out"), qp=h.p("qp"),
+                kp=h.p("kp"), qd=None, kd=None, ws=h.p("ws"))
+    args.update(ptr)
+    return _lib.load().ringattn_step_fwd(ctypes.byref(p) if p is not None else None, args["q"], args["k"],
+                                         args["v"], args["o"], args["lse"], args["out"], args["qp"], args["kp"],
+                                         args["qd"], args["kd"], mask, flags, args["ws"], ws_bytes, None)
+
+
+CASES = [
+    ("null problem", None, {}, {}, _lib.RA_ERR_INVALID),
+    ("hq not a multiple of hkv", _problem(hq=3), {}, {}, _lib.RA_ERR_INVALID),
+    ("head_dim 96", _problem(head_dim=96), {}, {}, _lib.RA_ERR_UNSUPPORTED),
+    ("dtype 7", _problem(dtype=7), {}, {}, _lib.RA_ERR_UNSUPPORTED),
+    ("negative sq", _problem(sq=-1), {}, {}, _lib.RA_ERR_INVALID),
+    ("zero batch", _problem(batch=0), {}, {}, _lib.RA_ERR_INVALID),
+    ("sk above the cap", _problem(sk=_lib.RA_MAX_SK + 1), {}, {}, _lib.RA_ERR_UNSUPPORTED),
+    ("stride not a multiple of 8", _problem(q_stride=(4 * 256 * 128, 256 * 128, 132)), {}, {}, _lib.RA_ERR_INVALID),
+    ("overlapping q rows", _problem(q_stride=(4 * 256 * 128, 256 * 128, 64)), {}, {}, _lib.RA_ERR_INVALID),
+    ("negative scale", _problem(softmax_scale=-1.0), {}, {}, _lib.RA_ERR_INVALID),
+    ("nan scale", _problem(softmax_scale=float("nan")), {}, {}, _lib.RA_ERR_INVALID),
+    ("mask mode 3", _problem(), {"mask": 3}, {}, _lib.RA_ERR_UNSUPPORTED),
+    ("doc mask without docs", _problem(), {"mask": 2}, {}, _lib.RA_ERR_INVALID),
+    ("unknown flag", _problem(), {"flags": 1 << 9}, {}, _lib.RA_ERR_INVALID),
+    ("null q", _problem(), {}, {"q": None}, _lib.RA_ERR_INVALID),
+    ("misaligned k", _problem(), {}, {"k": "misaligned"}, _lib.RA_ERR_INVALID),
+    ("null lse", _problem(), {}, {"lse": None}, _lib.RA_ERR_INVALID),
+    ("workspace too small", _problem(), {"ws_bytes": 16}, {}, _lib.RA_ERR_WORKSPACE),
+]
+
+
+@pytest.mark.parametrize("name,p,kw,ptr,status", CASES, ids=[c[0] for c in CASES])
+def test_step_fwd_validation(name, p, kw, ptr, status):
+    h = Host()
+    ptr = {k: (h.p(k, 2) if v == "misaligned" else v) for k, v in ptr.items()}
+    rc = step_fwd(h, p, **kw, **ptr)
+    assert rc == status, _lib.load().ringattn_last_error()
+    assert _lib.load().ringattn_last_error()
+    assert h.untouched()
+
+
+def test_empty_query_shard_is_a_no_op():
+    h = Host()
+    assert step_fwd(h, _problem(sq=0)) == _lib.RA_OK
+    assert h.untouched()
+
+
+def test_workspace_size_queries():
+    lib = _lib.load()
+    p = _problem(sq=1000, sk=130)
+    n = lib.ringattn_step_workspace_size(ctypes.byref(p))
+    assert n >= (16 + 3) * 16 and n % 256 == 0
+    assert lib.ringattn_step_workspace_size(ctypes.byref(_problem(head_dim=96))) == 0
+    d = _lib.RaRunDesc()
+    d.prob = _problem(sk=1024)
+    d.n_ranks, d.n_emulated, d.mask_mode, d.pass_ = 8, 1, 1, _lib.RA_PASS_FWD
+    ws = lib.ringattn_run_workspace_size(ctypes.byref(d))
+    blk = 1 * 2 * 1024 * 128 * 2
+    assert ws >= 2 * 2 * blk            # two staging slots of K and V
+    d.n_emulated = 9
+    assert lib.ringattn_run_workspace_size(ctypes.byref(d)) == 0
+
+
+def _run(h, d, **arrays):
+    lib = _lib.load()
+    pp = ctypes.POINTER(ctypes.c_void_p)
+
+    def arr(name, n):
+        a = (ctypes.c_void_p * n)(*[h.bufs[name].ctypes.data] * n)
+        arr.keep.append(a)
+        return ctypes.cast(a, pp)
+    arr.keep = []
+    n, r = d.n_ranks, max(d.n_emulated, 1)
+    A = dict(q=arr("q", r), k=arr("k", n), v=arr("v", n), o=arr("o", r), lse=arr("lse", r), out=arr("out", r),
+             qp=arr("qp", r), kp=arr("kp", n), qd=None, kd=None, do=None, delta=None, dq=None, dk=None, dv=None)
+    A.update(arrays)
+    return lib.ringattn_run(ctypes.byref(d), A["q"], A["k"], A["v"], A["o"], A["lse"], A["out"], A["qp"], A["kp"],
+                            A["qd"], A["kd"], A["do"], A["delta"], A["dq"], A["dk"], A["dv"], h.p("ws"), 1 << 30,
+                            None, None)
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("n_emulated", 9, _lib.RA_ERR_INVALID), ("n_ranks", 0, _lib.RA_ERR_INVALID),
+    ("start_step", 8, _lib.RA_ERR_INVALID), ("stop_step", -1, _lib.RA_ERR_INVALID),
+    ("pass_", 3, _lib.RA_ERR_INVALID), ("first_rank", 8, _lib.RA_ERR_INVALID),
+    ("flags", 1 << 12, _lib.RA_ERR_INVALID), ("mask_mode", 5, _lib.RA_ERR_UNSUPPORTED),
+])
+def test_run_validation(field, value, status):
+    h = Host()
+    d = _lib.RaRunDesc()
+    d.prob = _problem()
+    d.n_ranks, d.n_emulated, d.mask_mode, d.pass_ = 8, 1, 1, _lib.RA_PASS_FWD
+    setattr(d, field, value)
+    assert _run(h, d) == status, _lib.load().ringattn_last_error()
+    assert h.untouched()
+
+
+def test_run_rejects_strided_blocks_and_missing_backward_buffers():
+    h = Host()
+    d = _lib.RaRunDesc()
+    d.prob = _problem(kv_stride=(2 * 512 * 128, 512 * 128, 128))   # gaps between heads
+    d.n_ranks, d.n_emulated, d.mask_mode, d.pass_ = 4, 1, 1, _lib.RA_PASS_FWD
+    assert _run(h, d) == _lib.RA_ERR_INVALID
+    d.prob = _problem()
+    d.pass_ = _lib.RA_PASS_BWD
+    assert _run(h, d) == _lib.RA_ERR_INVALID          # no d_o / delta / dq / dk / dv
+    assert b"backward" in _lib.load().ringattn_last_error()
+    assert h.untouched()
