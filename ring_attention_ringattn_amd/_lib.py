@@ -9,7 +9,8 @@ from __future__ import annotations
 import ctypes
 import os
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libringattn.so")
+LIB_PATH = os.environ.get("RINGATTN_LIB") or os.path.join(os.path.dirname(os.path.abspath(__file__)),
+                                                         "libringattn.so")
 
 RA_OK, RA_ERR_INVALID, RA_ERR_UNSUPPORTED, RA_ERR_WORKSPACE, RA_ERR_HIP = 0, -1, -2, -3, -4
 RA_MASK_NONE, RA_MASK_CAUSAL, RA_MASK_DOC_CAUSAL = 0, 1, 2

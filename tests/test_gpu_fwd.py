@@ -94,7 +94,8 @@ def test_step_fwd_ragged_edges(case):
     print_case(f"step_fwd {case}")
     rng = np.random.default_rng(zlib.crc32(repr(case).encode()))
     wdt = torch.float32 if dtype == "f32" else torch.bfloat16
-    rnd = lambda *s: synthetic.bf16_round(rng.standard_normal(s).astype(np.float32)) if dtype == "bf16" \
+    # values as in the workloads: bf16 inputs N(0,1)*0.5, fp32 inputs N(0,1)
+    rnd = lambda *s: synthetic.bf16_round(0.5 * rng.standard_normal(s).astype(np.float32)) if dtype == "bf16" \
         else rng.standard_normal(s).astype(np.float32)
     q = rnd(B, hq, sq, d)
     k1, v1, k2, v2 = rnd(B, hkv, sk, d), rnd(B, hkv, sk, d), rnd(B, hkv, sk, d), rnd(B, hkv, sk, d)
