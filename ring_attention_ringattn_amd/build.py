@@ -54,6 +54,9 @@ def build(verbose: bool = False, out: str = LIB, defines=(), build_dir: str = BU
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")
     os.replace(tmp, out)
+    # resolve every symbol now: a kernel whose host launch stub was not emitted shows up here
+    import ctypes
+    ctypes.CDLL(out, mode=os.RTLD_NOW | os.RTLD_LOCAL)
     return out
 
 

@@ -1,6 +1,6 @@
 // Forward ring step, bf16 inputs, fp32 accumulation, on gfx950 MFMA.
 //
-// One workgroup = 4 waves = BM = 128*NB query rows of one (batch, query head);
+// One workgroup = 4 waves = BM = 128 query rows of one (batch, query head);
 // it walks the key/value block in tiles of BN = 64 keys, skipping tiles that
 // the mask hides entirely (per-tile position/document ranges).  Per tile:
 //
@@ -8,7 +8,8 @@
 //                         the wave's Q rows held in registers (B)
 //   mask + online softmax each lane owns whole query columns of S^T, so the
 //                         running max/sum need one cross-lane exchange
-//   O^T += V^T P^T        V^T from LDS (A); P^T straight from the S^T
+//   O^T += V^T P^T        V^T read from the row-major V tile with the LDS
+//                         transpose read (A); P^T straight from the S^T
 //                         accumulator registers (B), converted to bf16
 //
 // Making the S^T accumulator usable as the P^T operand without a shuffle:
@@ -19,16 +20,21 @@
 // keys, which is exactly the operand layout; the keys of the V^T operand are
 // then read in natural order.
 //
-// Pipeline: the next tile's K/V are loaded from HBM into registers at the top
-// of an iteration and stored into the other half of a double-buffered LDS at
-// its bottom, so one barrier per tile orders everything.  Two workgroups fit
-// on a CU (<= 256 VGPRs per lane), so one workgroup's softmax overlaps the
-// other's MFMAs.
+// Data movement: K and V tiles go from HBM straight into LDS with buffer
+// loads (no register staging; the buffer range zero-fills keys past the end
+// of the block), double-buffered so the next tile streams in during the
+// current one's MFMAs; one barrier per tile.  Tiles are stored row-major with
+// the 16-byte units of each row XOR-swizzled by the row index, so both the
+// K operand reads (16 lanes, 16 different rows, one column) and the V
+// transpose reads (4 rows x 64 bytes per half-wave) hit distinct banks.
+// Two workgroups fit on a CU, so one workgroup's softmax overlaps the other's
+// MFMAs.
 //
 // Online softmax with a lazily updated maximum: the running maximum m only
 // moves when a tile's maximum exceeds it by more than RESCALE_SLACK (log2
 // units), so exp2(s - m) <= 2^RESCALE_SLACK and the accumulator is rescaled
-// only on those (rare) tiles; the result is the same up to rounding.
+// only on those (rare) tiles; the result is the same up to rounding.  The
+// row sum is accumulated in fp32.
 //
 // The step's normalised partial (O_t = acc / l, LSE_t = m ln2 + ln l) is
 // merged into the running (o_acc, lse) in the epilogue with the exact
@@ -39,31 +45,66 @@ namespace ra {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+#define RA_LDS __attribute__((address_space(3)))
 
 namespace {
 
 constexpr int BN = 64;      // keys per tile (== TILE)
 constexpr int NWAVES = 4;
+constexpr int BM = NWAVES * 32;   // query rows per workgroup (32 per wave)
 constexpr int LIST = 256;   // tile-list chunk (one tile per thread when building it)
 constexpr float LN2 = 0.69314718055994530942f;
 constexpr float RESCALE_SLACK = 8.0f;
+constexpr int RSRC_WORD3 = 0x00020000;   // raw (untyped) buffer access on the gfx9 family
 
-template <int D, int NB>
+template <int D>
 struct Cfg {
-  static constexpr int WQ = 32 * NB;       // query rows per wave
-  static constexpr int BM = NWAVES * WQ;   // query rows per workgroup
-  static constexpr int KS = D + 8;         // K tile row stride in LDS (elements)
-  static constexpr int VS = BN + 8;        // V^T tile row stride in LDS (elements)
-  static constexpr int KCH = BN * D / 8 / 256;        // 16-byte K chunks per thread per tile
-  static constexpr int NVQ = (BN / 4) * (D / 8);        // 4-key x 8-dim V blocks per tile
-  static constexpr int VQ = (NVQ + 255) / 256;          // ... per thread (threads past NVQ idle)
+  static constexpr int U = D / 8;                    // 16-byte units per row
+  static constexpr int CHUNKS = BN * D * 2 / 1024;   // 1 KB buffer->LDS chunks per tile
+  static constexpr int CPW = CHUNKS / NWAVES;        // ... per wave
 };
 
 __device__ __forceinline__ int swap23(int m) { return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1); }
 
+// Unit swizzles of the row-major tiles (see the file comment).
+template <int D>
+__device__ __forceinline__ int kswz(int r) { return D == 128 ? (r & 15) : ((r >> 1) & 7); }
+template <int D>
+__device__ __forceinline__ int vswz(int r) { return D == 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1); }
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// gfx950-only builtins live in device functions: used directly in a kernel
+// template body they make clang drop the kernel's host-side launch stub.
+
+// Copy 16 bytes per lane from base + voff into LDS at dst + 16*lane; bytes at
+// or past base + nbytes read as zero (buffer range check).
+__device__ __forceinline__ void dma16(const void* base, int nbytes, RA_LDS void* dst, int voff) {
+  const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, nbytes, RSRC_WORD3);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, dst, 16, voff, 0, 0, 0);
+}
+
+// LDS transpose read of 4 bf16 (see the V operand comment in the kernel).
+__device__ __forceinline__ s16x4 lds_read_tr16(const __bf16* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((RA_LDS s16x4*)p);
+}
+
+
+// Both lanes of a (j, j+32) pair get the pair's maximum / sum.
+__device__ __forceinline__ float pair_max(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair_sum(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
 
 // Merge weights of (lse_a) (+) (lse_b): returns lse, weights of a and b.
 __device__ __forceinline__ void lse_combine(float la, float lb, float& lse, float& wa, float& wb) {
@@ -98,28 +139,28 @@ __device__ __forceinline__ void map_block(int n_qt, int hq, int hkv, int total, 
 
 }  // namespace
 
-template <int D, int NB>
-__global__ __launch_bounds__(256, NB == 1 ? 2 : 1) void fwd_bf16_kernel(FwdArgs a) {
-  using C = Cfg<D, NB>;
-  __shared__ __attribute__((aligned(16))) __bf16 Ks[2][BN * C::KS];
-  __shared__ __attribute__((aligned(16))) __bf16 Vt[2][D * C::VS];
+template <int D>
+__global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs a) {
+  using C = Cfg<D>;
+  __shared__ __attribute__((aligned(1024))) __bf16 Ks[2][BN * D];
+  __shared__ __attribute__((aligned(1024))) __bf16 Vs[2][BN * D];
   __shared__ __attribute__((aligned(16))) int kvp[2][BN];
   __shared__ __attribute__((aligned(16))) int kvd[2][BN];
   __shared__ int list[LIST];
   __shared__ int wave_cnt[NWAVES];
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, g = lane >> 5, j = lane & 31;
-  const int n_qt = (a.sq + C::BM - 1) / C::BM;
+  const int n_qt = (a.sq + BM - 1) / BM;
   int b, h, qt;
   map_block(n_qt, a.hq, a.hkv, n_qt * a.hq * a.B, b, h, qt);
   const int kvh = (h * a.hkv) / a.hq;
-  const int q0 = qt * C::BM;
+  const int q0 = qt * BM;
   const int mask = a.mask;
 
   // Position/document range of this query tile (valid rows only).
   TileRange qr{0x7fffffff, (int)0x80000000, 0x7fffffff, (int)0x80000000};
   {
-    const int t_end = min(n_tiles(a.sq), (q0 + C::BM) / TILE);
+    const int t_end = min(n_tiles(a.sq), (q0 + BM) / TILE);
     for (int t = q0 / TILE; t < t_end; ++t) {
       const TileRange r = a.q_tiles[t];
       qr.min_pos = min(qr.min_pos, r.min_pos); qr.max_pos = max(qr.max_pos, r.max_pos);
@@ -127,62 +168,55 @@ __global__ __launch_bounds__(256, NB == 1 ? 2 : 1) void fwd_bf16_kernel(FwdArgs 
     }
   }
 
-  // This wave's query rows: Q fragments (MFMA B operand) and positions.
+  // This wave's 32 query rows: Q fragments (MFMA B operand) and positions.
   const __bf16* qptr = (const __bf16*)a.q + b * a.qs.b + h * a.qs.h;
-  bf16x8 qf[NB][D / 16];
-  int qpos[NB], qdoc[NB];
+  const int qrow = q0 + wave * 32 + j;
+  const bool qvalid = qrow < a.sq;
+  bf16x8 qf[D / 16];
 #pragma unroll
-  for (int nb = 0; nb < NB; ++nb) {
-    const int row = q0 + wave * C::WQ + nb * 32 + j;
-    const bool valid = row < a.sq;
-#pragma unroll
-    for (int ks = 0; ks < D / 16; ++ks) {
-      bf16x8 z = {};
-      qf[nb][ks] = valid ? *(const bf16x8*)(qptr + row * a.qs.s + ks * 16 + g * 8) : z;
-    }
-    qpos[nb] = valid ? a.q_pos[row] : -1;
-    qdoc[nb] = (valid && mask == MASK_DOC_CAUSAL) ? a.q_doc[row] : 0;
+  for (int ks = 0; ks < D / 16; ++ks) {
+    bf16x8 z = {};
+    qf[ks] = qvalid ? *(const bf16x8*)(qptr + qrow * a.qs.s + ks * 16 + g * 8) : z;
   }
+  const int qpos = qvalid ? a.q_pos[qrow] : -1;
+  const int qdoc = (qvalid && mask == MASK_DOC_CAUSAL) ? a.q_doc[qrow] : 0;
 
-  float m_run[NB], l_run[NB];
-  f32x16 acc[NB][D / 32];
+  float m_run = -INFINITY, l_run = 0.f;
+  f32x16 acc[D / 32];
 #pragma unroll
-  for (int nb = 0; nb < NB; ++nb) {
-    m_run[nb] = -INFINITY;
-    l_run[nb] = 0.f;
-#pragma unroll
-    for (int db = 0; db < D / 32; ++db) acc[nb][db] = f32x16{};
-  }
+  for (int db = 0; db < D / 32; ++db) acc[db] = f32x16{};
 
   const __bf16* kptr = (const __bf16*)a.k + b * a.kvs.b + kvh * a.kvs.h;
   const __bf16* vptr = (const __bf16*)a.v + b * a.kvs.b + kvh * a.kvs.h;
+  const int rsb = (int)(a.kvs.s * 2);   // bytes between consecutive keys
   const int nkt = n_tiles(a.sk);
   const bool no_skip = (a.flags & FLAG_NO_SKIP) != 0;
   const float sl2 = a.scale_log2;
 
-  // register staging of one tile on its way from HBM to LDS
-  bf16x8 kreg[C::KCH];
-  bf16x8 vreg[C::VQ][4];
+  // Per-lane byte offsets (within a tile) of this lane's 16-byte unit of each
+  // of the wave's CPW buffer->LDS chunks: chunk q = c*4 + wave covers LDS
+  // units [64q, 64q+64); unit p holds row p/U, logical column (p%U) ^ swz(row).
+  int voff_k[C::CPW], voff_v[C::CPW];
+#pragma unroll
+  for (int c = 0; c < C::CPW; ++c) {
+    const int p = (c * NWAVES + wave) * 64 + lane;
+    const int r = p / C::U, pu = p % C::U;
+    voff_k[c] = r * rsb + (pu ^ kswz<D>(r)) * 16;
+    voff_v[c] = r * rsb + (pu ^ vswz<D>(r)) * 16;
+  }
   int preg = POS_INVALID, dreg = 0;
 
-  auto load_tile = [&](int kbase) {
+  // Start streaming tile `tile` into LDS buffer `buf`.
+  auto issue_tile = [&] __device__(int tile, int buf) {
+    const int kbase = tile * BN;
+    const int rows = min(BN, a.sk - kbase);
+    const __bf16* kb = kptr + (size_t)kbase * a.kvs.s;
+    const __bf16* vb = vptr + (size_t)kbase * a.kvs.s;
 #pragma unroll
-    for (int i = 0; i < C::KCH; ++i) {
-      const int c = tid + 256 * i;
-      const int key = c / (D / 8), c8 = c % (D / 8);
-      bf16x8 z = {};
-      kreg[i] = kbase + key < a.sk ? *(const bf16x8*)(kptr + (kbase + key) * a.kvs.s + c8 * 8) : z;
-    }
-#pragma unroll
-    for (int i = 0; i < C::VQ; ++i) {
-      const int qd = tid + 256 * i;
-      const int kq = qd % (BN / 4), c8 = qd / (BN / 4);
-#pragma unroll
-      for (int e4 = 0; e4 < 4; ++e4) {
-        const int key = kbase + kq * 4 + e4;
-        bf16x8 z = {};
-        vreg[i][e4] = (qd < C::NVQ && key < a.sk) ? *(const bf16x8*)(vptr + key * a.kvs.s + c8 * 8) : z;
-      }
+    for (int c = 0; c < C::CPW; ++c) {
+      const int q = c * NWAVES + wave;
+      dma16(kb, rows * rsb, (RA_LDS void*)&Ks[buf][q * 512], voff_k[c]);
+      dma16(vb, rows * rsb, (RA_LDS void*)&Vs[buf][q * 512], voff_v[c]);
     }
     if (tid < BN) {
       const int key = kbase + tid;
@@ -191,28 +225,12 @@ __global__ __launch_bounds__(256, NB == 1 ? 2 : 1) void fwd_bf16_kernel(FwdArgs 
       dreg = (ok && mask == MASK_DOC_CAUSAL) ? a.kv_doc[key] : 0;
     }
   };
-  auto store_tile = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < C::KCH; ++i) {
-      const int c = tid + 256 * i;
-      const int key = c / (D / 8), c8 = c % (D / 8);
-      *(bf16x8*)(&Ks[buf][key * C::KS + c8 * 8]) = kreg[i];
-    }
-#pragma unroll
-    for (int i = 0; i < C::VQ; ++i) {
-      const int qd = tid + 256 * i;
-      const int kq = qd % (BN / 4), c8 = qd / (BN / 4);
-      if (qd >= C::NVQ) break;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        bf16x4 col = {vreg[i][0][e], vreg[i][1][e], vreg[i][2][e], vreg[i][3][e]};
-        *(bf16x4*)(&Vt[buf][(c8 * 8 + e) * C::VS + kq * 4]) = col;
-      }
-    }
+  auto finish_tile = [&] __device__(int buf) {
     if (tid < BN) {
       kvp[buf][tid] = preg;
       kvd[buf][tid] = dreg;
     }
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this thread's buffer->LDS loads have landed
   };
 
   for (int c0 = 0; c0 < nkt; c0 += LIST) {
@@ -238,103 +256,107 @@ __global__ __launch_bounds__(256, NB == 1 ? 2 : 1) void fwd_bf16_kernel(FwdArgs 
     __syncthreads();
     if (total == 0) continue;
 
-    load_tile((list[0] & 0xffffff) * BN);
-    store_tile(0);
+    issue_tile(__builtin_amdgcn_readfirstlane(list[0]) & 0xffffff, 0);
+    finish_tile(0);
     __syncthreads();
 
     for (int li = 0; li < total; ++li) {
       const int buf = li & 1;
-      const int ent = list[li];
+      // the list entry is workgroup-uniform: keep it scalar so the branches on it stay branches
+      const int ent = __builtin_amdgcn_readfirstlane(list[li]);
       const bool partial = (ent >> 24) == TILE_PARTIAL;
+      const int kvalid = a.sk - (ent & 0xffffff) * BN;   // keys of this tile that exist (>= BN: all)
       const bool more = li + 1 < total;
-      if (more) load_tile((list[li + 1] & 0xffffff) * BN);
+      if (more) issue_tile(__builtin_amdgcn_readfirstlane(list[li + 1]) & 0xffffff, buf ^ 1);
 
       // ---- S^T = K Q^T (raw scores) ----
-      f32x16 s[2][NB];
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb) s[mb][nb] = f32x16{};
+      f32x16 s[2];
+      s[0] = f32x16{};
+      s[1] = f32x16{};
 #pragma unroll
       for (int ks = 0; ks < D / 16; ++ks) {
 #pragma unroll
         for (int mb = 0; mb < 2; ++mb) {
-          const bf16x8 kf = *(const bf16x8*)(&Ks[buf][(mb * 32 + swap23(j)) * C::KS + ks * 16 + g * 8]);
-#pragma unroll
-          for (int nb = 0; nb < NB; ++nb)
-            s[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[nb][ks], s[mb][nb], 0, 0, 0);
+          const int r = mb * 32 + swap23(j);
+          const bf16x8 kf = *(const bf16x8*)(&Ks[buf][r * D + (((ks * 2 + g) ^ kswz<D>(r)) * 8)]);
+          s[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], s[mb], 0, 0, 0);
         }
       }
 
-      // ---- mask, online softmax ----
+      // ---- mask (partial tiles only), online softmax ----
       // lane (g, j), value v of block mb holds key mb*32 + 16*(v/8) + 8*g + v%8 for query j.
+      if (partial) {
+        asm volatile("" ::: "memory");   // keep this a real branch: full tiles must not pay for masking
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb) {
-        if (partial) {
+        for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-          for (int mb = 0; mb < 2; ++mb)
+          for (int hh = 0; hh < 2; ++hh) {
+            const int base = mb * 32 + 16 * hh + 8 * g;
+            const i32x4 p0 = *(const i32x4*)&kvp[buf][base], p1 = *(const i32x4*)&kvp[buf][base + 4];
+            const i32x4 d0 = *(const i32x4*)&kvd[buf][base], d1 = *(const i32x4*)&kvd[buf][base + 4];
 #pragma unroll
-            for (int hh = 0; hh < 2; ++hh) {
-              const int base = mb * 32 + 16 * hh + 8 * g;
-#pragma unroll
-              for (int e = 0; e < 8; ++e) {
-                const int kp = kvp[buf][base + e];
-                bool ok = kp != POS_INVALID;
-                if (mask != MASK_NONE) ok = ok && kp <= qpos[nb];
-                if (mask == MASK_DOC_CAUSAL) ok = ok && kvd[buf][base + e] == qdoc[nb];
-                if (!ok) s[mb][nb][hh * 8 + e] = -INFINITY;
-              }
+            for (int e = 0; e < 8; ++e) {
+              const int kp = e < 4 ? p0[e] : p1[e - 4];
+              const int kd = e < 4 ? d0[e] : d1[e - 4];
+              bool ok = base + e < kvalid;
+              if (mask != MASK_NONE) ok = ok && kp <= qpos;
+              if (mask == MASK_DOC_CAUSAL) ok = ok && kd == qdoc;
+              s[mb][hh * 8 + e] = ok ? s[mb][hh * 8 + e] : -INFINITY;
             }
-        }
-        float mx = -INFINITY;
-#pragma unroll
-        for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-          for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s[mb][nb][v]);
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
-        const float mt = mx * sl2;   // tile maximum, scaled log2 units (-inf stays -inf)
-        // move the running maximum only when this tile would overflow the slack
-        const bool grow = mt > m_run[nb] + RESCALE_SLACK;
-        if (__any(grow)) {
-          // lanes that do not grow keep their maximum (alpha = 1; their m may still be -inf)
-          const float alpha = grow ? fast_exp2(m_run[nb] - mt) : 1.f;   // 0 when growing from -inf
-          m_run[nb] = grow ? mt : m_run[nb];
-          l_run[nb] *= alpha;
-#pragma unroll
-          for (int db = 0; db < D / 32; ++db) acc[nb][db] *= alpha;
-        }
-        const float m_use = m_run[nb] == -INFINITY ? 0.f : m_run[nb];
-        float rs = 0.f;
-#pragma unroll
-        for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-          for (int v = 0; v < 16; ++v) {
-            const float p = fast_exp2(__builtin_fmaf(s[mb][nb][v], sl2, -m_use));
-            s[mb][nb][v] = p;
-            rs += p;
           }
-        l_run[nb] += rs;
       }
+      float mx = -INFINITY;
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s[mb][v]);
+      const float mt = pair_max(mx) * sl2;   // tile maximum, scaled log2 units (-inf stays -inf)
+      // move the running maximum only when this tile would overflow the slack
+      const bool grow = mt > m_run + RESCALE_SLACK;
+      if (__any(grow)) {
+        // lanes that do not grow keep their maximum (alpha = 1; their m may still be -inf)
+        const float alpha = grow ? fast_exp2(m_run - mt) : 1.f;   // 0 when growing from -inf
+        m_run = grow ? mt : m_run;
+        l_run *= alpha;
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) acc[db] *= alpha;
+      }
+      const float neg_m = m_run == -INFINITY ? 0.f : -m_run;
+      // probabilities: fp32 for the row sum (the LSE needs it; a sum of the bf16-rounded
+      // values would be off by up to 2^-9 relative), bf16 for the PV product
+      bf16x8 pf[4];
+      float rs = 0.f;
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float p = fast_exp2(__builtin_fmaf(s[kk >> 1][(kk & 1) * 8 + e], sl2, neg_m));
+          rs += p;
+          pf[kk][e] = (__bf16)p;
+        }
+      l_run += rs;
 
-      // ---- O^T += V^T P^T ----
-      bf16x8 pf[NB][4];
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk)
-#pragma unroll
-          for (int e = 0; e < 8; ++e) pf[nb][kk][e] = (__bf16)s[kk >> 1][nb][(kk & 1) * 8 + e];
+      // ---- O^T += V^T P^T, V^T from the row-major tile by transpose reads ----
+      // 16-lane group G of lane l: source lane s = l%16 points at key
+      // kk*16 + (G/2)*8 + half*4 + s/4, dims db*32 + (G%2)*16 + 4*(s%4) .. +3.
+      const int G = lane >> 4, sl = lane & 15;
 #pragma unroll
       for (int db = 0; db < D / 32; ++db) {
+        const int dcol = db * 32 + (G & 1) * 16 + 4 * (sl & 3);
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) {
-          const bf16x8 vf = *(const bf16x8*)(&Vt[buf][(db * 32 + j) * C::VS + kk * 16 + g * 8]);
+          s16x4 half[2];
 #pragma unroll
-          for (int nb = 0; nb < NB; ++nb)
-            acc[nb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[nb][kk], acc[nb][db], 0, 0, 0);
+          for (int hf = 0; hf < 2; ++hf) {
+            const int key = kk * 16 + (G >> 1) * 8 + hf * 4 + (sl >> 2);
+            const int off = key * D + (((dcol >> 3) ^ vswz<D>(key)) << 3) + (dcol & 7);
+            half[hf] = lds_read_tr16(&Vs[buf][off]);
+          }
+          const bf16x8 vf = __builtin_bit_cast(bf16x8, __builtin_shufflevector(half[0], half[1], 0, 1, 2, 3, 4, 5, 6, 7));
+          acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[kk], acc[db], 0, 0, 0);
         }
       }
-      if (more) store_tile(buf ^ 1);
+      if (more) finish_tile(buf ^ 1);
       __syncthreads();
     }
   }
@@ -342,53 +364,43 @@ __global__ __launch_bounds__(256, NB == 1 ? 2 : 1) void fwd_bf16_kernel(FwdArgs 
   // ---- epilogue: normalise, merge into (o_acc, lse), optionally write out ----
   const bool first = (a.flags & FLAG_FIRST) != 0;
   const bool last = (a.flags & FLAG_LAST) != 0 && a.out != nullptr;
+  const float l_tot = pair_sum(l_run);
+  if (!qvalid) return;
+  const float lse_t = l_tot > 0.f ? (m_run + log2f(l_tot)) * LN2 : -INFINITY;
+  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+  const size_t orow = ((size_t)b * a.hq + h) * a.sq + qrow;
+  float lse_new = lse_t, w_p = 0.f, w_t = inv;
+  if (!first) {
+    float wp, wt;
+    lse_combine(a.lse[orow], lse_t, lse_new, wp, wt);
+    w_p = wp;
+    w_t = wt * inv;
+  }
+  float* op = a.o_acc + orow * D;
+  __bf16* outp = last ? (__bf16*)a.out + b * a.qs.b + h * a.qs.h + qrow * a.qs.s : nullptr;
 #pragma unroll
-  for (int nb = 0; nb < NB; ++nb) {
-    const float l_tot = l_run[nb] + __shfl_xor(l_run[nb], 32);
-    const int row = q0 + wave * C::WQ + nb * 32 + j;
-    if (row >= a.sq) continue;
-    const float lse_t = l_tot > 0.f ? (m_run[nb] + log2f(l_tot)) * LN2 : -INFINITY;
-    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-    const size_t orow = ((size_t)b * a.hq + h) * a.sq + row;
-    float lse_new = lse_t, w_p = 0.f, w_t = inv;
-    if (!first) {
-      float wp, wt;
-      lse_combine(a.lse[orow], lse_t, lse_new, wp, wt);
-      w_p = wp;
-      w_t = wt * inv;
-    }
-    float* op = a.o_acc + orow * D;
-    __bf16* outp = last ? (__bf16*)a.out + b * a.qs.b + h * a.qs.h + row * a.qs.s : nullptr;
+  for (int db = 0; db < D / 32; ++db) {
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db) {
-#pragma unroll
-      for (int vh = 0; vh < 4; ++vh) {
-        const int d = db * 32 + vh * 8 + g * 4;
-        f32x4 o = {acc[nb][db][vh * 4 + 0] * w_t, acc[nb][db][vh * 4 + 1] * w_t,
-                   acc[nb][db][vh * 4 + 2] * w_t, acc[nb][db][vh * 4 + 3] * w_t};
-        if (!first) o += w_p * *(const f32x4*)(op + d);
-        *(f32x4*)(op + d) = o;
-        if (last) {
-          bf16x4 ob = {(__bf16)o[0], (__bf16)o[1], (__bf16)o[2], (__bf16)o[3]};
-          *(bf16x4*)(outp + d) = ob;
-        }
+    for (int vh = 0; vh < 4; ++vh) {
+      const int d = db * 32 + vh * 8 + g * 4;
+      f32x4 o = {acc[db][vh * 4 + 0] * w_t, acc[db][vh * 4 + 1] * w_t, acc[db][vh * 4 + 2] * w_t,
+                 acc[db][vh * 4 + 3] * w_t};
+      if (!first) o += w_p * *(const f32x4*)(op + d);
+      *(f32x4*)(op + d) = o;
+      if (last) {
+        bf16x4 ob = {(__bf16)o[0], (__bf16)o[1], (__bf16)o[2], (__bf16)o[3]};
+        *(bf16x4*)(outp + d) = ob;
       }
     }
-    if (g == 0) a.lse[orow] = lse_new;
   }
+  if (g == 0) a.lse[orow] = lse_new;
 }
 
-#ifndef RA_FWD_NB
-#define RA_FWD_NB 1
-#endif
-
 hipError_t launch_fwd_bf16(const FwdArgs& a, int d, hipStream_t st) {
-  constexpr int NB = RA_FWD_NB;
-  const int bm = NWAVES * 32 * NB;
-  const long blocks = (long)((a.sq + bm - 1) / bm) * a.hq * a.B;
+  const long blocks = (long)((a.sq + BM - 1) / BM) * a.hq * a.B;
   if (blocks == 0) return hipSuccess;
-  if (d == 128) fwd_bf16_kernel<128, NB><<<(unsigned)blocks, 256, 0, st>>>(a);
-  else fwd_bf16_kernel<64, NB><<<(unsigned)blocks, 256, 0, st>>>(a);
+  if (d == 128) fwd_bf16_kernel<128><<<(unsigned)blocks, 256, 0, st>>>(a);
+  else fwd_bf16_kernel<64><<<(unsigned)blocks, 256, 0, st>>>(a);
   return hipGetLastError();
 }
 
