@@ -1,8 +1,437 @@
-// Backward ring step, bf16 inputs, on gfx950 MFMA (placeholder until the MFMA kernels land).
-#include "ra_internal.h"
+// Backward ring step, bf16 inputs, fp32 accumulation, on gfx950 MFMA.
+//
+// The attention weights are recomputed from the final LSE (no merge is
+// needed in the backward: P = exp(s - LSE) is already the globally
+// normalised weight), with the loss L = sum(O * dO):
+//   dV = P^T dO,  dP = dO V^T,  dS = P (dP - delta),  dQ = scale dS K,
+//   dK = scale dS^T Q,          delta = rowsum(dO * O).
+// Two kernels, so that every output has one writer (deterministic, no
+// atomics):
+//
+// bwd_dkdv_kernel: a workgroup owns 128 keys of one kv head (32 per wave; the
+//   wave's K and V rows stay in registers as MFMA B operands) and streams the
+//   GQA group's query tiles (64 rows of Q, dO, LSE, delta, positions) through
+//   double-buffered swizzled LDS.  Per 32 query rows:
+//     S  = Q K^T, dP = dO V^T          (Q, dO rows from LDS as A operands,
+//                                        rows loaded in swap23 order)
+//     P  = exp2(S c - LSE log2 e), dS = P (dP - delta)
+//     dV += P^T dO, dK += dS^T Q       (P, dS straight from registers as A
+//                                        operands; dO, Q by transpose reads)
+//   then dk, dv (fp32, owned by this workgroup) += the sums.
+//
+// bwd_dq_kernel: a workgroup owns 128 query rows of one query head (32 per
+//   wave; Q and dO rows in registers as B operands) and streams 64-key K/V
+//   tiles like the forward kernel.  Per tile:
+//     S^T = K Q^T, dP^T = V dO^T, P^T, dS^T (as above, transposed)
+//     dQ^T += K^T dS^T                  (K^T by transpose reads, dS^T from
+//                                        registers)
+//   then dq += scale dQ.
+// Fully masked tile pairs are skipped in both kernels.
+#include "mfma_tile.h"
 
 namespace ra {
 
-hipError_t launch_bwd_bf16(const BwdArgs&, int, hipStream_t) { return hipErrorNotSupported; }
+namespace {
+
+constexpr int NWAVES = 4;
+constexpr int BQ = 64;                 // query rows per staged tile (dK/dV kernel)
+constexpr int BK = NWAVES * 32;        // keys per workgroup (dK/dV kernel)
+constexpr int BKT = 64;                // keys per staged tile (dQ kernel)
+constexpr int BMQ = NWAVES * 32;       // query rows per workgroup (dQ kernel)
+constexpr int LIST = 256;
+
+// Compact the indices i in [c0, c0 + LIST) with cls(i) != EMPTY into `list`
+// (entries i | cls << 24); returns their number.  All threads must call it.
+template <typename F>
+__device__ __forceinline__ int build_list(int c0, int n, F cls_of, int* list, int* wave_cnt) {
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int i = c0 + tid;
+  const int cls = i < n ? cls_of(i) : TILE_EMPTY;
+  const unsigned long long bal = __ballot(cls != TILE_EMPTY);
+  const int my = __popcll(bal & ((1ull << lane) - 1ull));
+  if (lane == 0) wave_cnt[wave] = __popcll(bal);
+  __syncthreads();
+  int off = 0, total = 0;
+#pragma unroll
+  for (int w = 0; w < NWAVES; ++w) {
+    const int c = wave_cnt[w];
+    off += (w < wave) ? c : 0;
+    total += c;
+  }
+  if (cls != TILE_EMPTY) list[off + my] = i | (cls << 24);
+  __syncthreads();
+  return total;
+}
+
+}  // namespace
+
+// ------------------------------------------------------------------ dK / dV
+template <int D>
+__global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
+  constexpr int CPW = BQ * D * 2 / 1024 / NWAVES;   // buffer->LDS chunks per wave per tile
+  __shared__ __attribute__((aligned(1024))) __bf16 Qs[2][BQ * D];
+  __shared__ __attribute__((aligned(1024))) __bf16 Os[2][BQ * D];    // dO
+  __shared__ __attribute__((aligned(16))) float lse2s[2][BQ];         // LSE log2(e); +inf: row sees nothing
+  __shared__ __attribute__((aligned(16))) float dels[2][BQ];
+  __shared__ __attribute__((aligned(16))) int qps[2][BQ];
+  __shared__ __attribute__((aligned(16))) int qds[2][BQ];
+  __shared__ int list[LIST];
+  __shared__ int wave_cnt[NWAVES];
+
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, g = lane >> 5, j = lane & 31;
+  const int n_kt = (a.sk + BK - 1) / BK;
+  int r = xcd_logical(blockIdx.x, n_kt * a.hkv * a.B);
+  const int kt = r % n_kt; r /= n_kt;
+  const int kvh = r % a.hkv, b = r / a.hkv;
+  const int k0 = kt * BK;
+  const int mask = a.mask;
+  const int grp = a.hq / a.hkv;
+
+  // key range of the workgroup
+  TileRange kr{0x7fffffff, (int)0x80000000, 0x7fffffff, (int)0x80000000};
+  for (int t = k0 / TILE; t < min(n_tiles(a.sk), (k0 + BK) / TILE); ++t) {
+    const TileRange x = a.kv_tiles[t];
+    kr.min_pos = min(kr.min_pos, x.min_pos); kr.max_pos = max(kr.max_pos, x.max_pos);
+    kr.min_doc = min(kr.min_doc, x.min_doc); kr.max_doc = max(kr.max_doc, x.max_doc);
+  }
+  const bool kcomplete = k0 + BK <= a.sk;
+
+  // this wave's 32 keys: K and V rows as MFMA B operands (lane j = key)
+  const int key = k0 + wave * 32 + j;
+  const bool kvalid = key < a.sk;
+  const size_t koff = b * a.kvs.b + kvh * a.kvs.h + (size_t)key * a.kvs.s;
+  bf16x8 kf[D / 16], vf[D / 16];
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks) {
+    bf16x8 z = {};
+    kf[ks] = kvalid ? *(const bf16x8*)((const __bf16*)a.k + koff + ks * 16 + g * 8) : z;
+    vf[ks] = kvalid ? *(const bf16x8*)((const __bf16*)a.v + koff + ks * 16 + g * 8) : z;
+  }
+  const int kpos = kvalid ? a.kv_pos[key] : POS_INVALID;
+  const int kdoc = (kvalid && mask == MASK_DOC_CAUSAL) ? a.kv_doc[key] : 0;
+
+  f32x16 dk[D / 32], dv[D / 32];
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db) {
+    dk[db] = f32x16{};
+    dv[db] = f32x16{};
+  }
+
+  const int n_qt = n_tiles(a.sq);
+  const int rsb = (int)(a.qs.s * 2);
+  const float sl2 = a.scale_log2;
+  int voff[CPW];
+#pragma unroll
+  for (int c = 0; c < CPW; ++c) voff[c] = chunk_voff<D>(c * NWAVES + wave, lane, rsb);
+  float sreg = 0.f;
+  int ireg = 0;
+
+  // stage query tile `item` (= query head in group * n_qt + tile) into buffer `buf`
+  auto issue_tile = [&] __device__(int item, int buf) {
+    const int hh = item / n_qt, qt = item % n_qt;
+    const int h = kvh * grp + hh;
+    const int q0 = qt * BQ;
+    const int rows = min(BQ, a.sq - q0);
+    const size_t base = b * a.qs.b + h * a.qs.h + (size_t)q0 * a.qs.s;
+#pragma unroll
+    for (int c = 0; c < CPW; ++c) {
+      const int q = c * NWAVES + wave;
+      dma16((const __bf16*)a.q + base, rows * rsb, (RA_LDS void*)&Qs[buf][q * 512], voff[c]);
+      dma16((const __bf16*)a.d_o + base, rows * rsb, (RA_LDS void*)&Os[buf][q * 512], voff[c]);
+    }
+    const int row = tid & 63, part = tid >> 6;
+    const bool ok = row < rows;
+    const size_t lrow = ((size_t)b * a.hq + h) * a.sq + q0 + row;
+    if (part == 0) {
+      const float l = ok ? a.lse[lrow] : -INFINITY;
+      sreg = l == -INFINITY ? INFINITY : l * LOG2E;
+    } else if (part == 1) {
+      sreg = ok ? a.delta[lrow] : 0.f;
+    } else if (part == 2) {
+      ireg = ok ? a.q_pos[q0 + row] : -1;
+    } else {
+      ireg = (ok && mask == MASK_DOC_CAUSAL) ? a.q_doc[q0 + row] : 0;
+    }
+  };
+  auto finish_tile = [&] __device__(int buf) {
+    const int row = tid & 63, part = tid >> 6;
+    if (part == 0) lse2s[buf][row] = sreg;
+    else if (part == 1) dels[buf][row] = sreg;
+    else if (part == 2) qps[buf][row] = ireg;
+    else qds[buf][row] = ireg;
+    wait_vmem();
+  };
+
+  const int n_items = grp * n_qt;
+  const bool no_skip = (a.flags & FLAG_NO_SKIP) != 0;
+  for (int c0 = 0; c0 < n_items; c0 += LIST) {
+    const int total = build_list(c0, n_items, [&] __device__(int it) {
+      int c = classify(a.q_tiles[it % n_qt], kr, kcomplete, mask);
+      return (no_skip && c == TILE_EMPTY) ? (int)TILE_PARTIAL : c;
+    }, list, wave_cnt);
+    if (total == 0) continue;
+    issue_tile(__builtin_amdgcn_readfirstlane(list[0]) & 0xffffff, 0);
+    finish_tile(0);
+    __syncthreads();
+
+    for (int li = 0; li < total; ++li) {
+      const int buf = li & 1;
+      const int ent = __builtin_amdgcn_readfirstlane(list[li]);
+      const bool partial = (ent >> 24) == TILE_PARTIAL;
+      const bool more = li + 1 < total;
+      if (more) issue_tile(__builtin_amdgcn_readfirstlane(list[li + 1]) & 0xffffff, buf ^ 1);
+
+#pragma unroll 1
+      for (int mb = 0; mb < 2; ++mb) {
+        f32x16 s = {}, dp = {};
+#pragma unroll
+        for (int ks = 0; ks < D / 16; ++ks) {
+          const int off = tile_off<D>(mb * 32 + swap23(j), ks * 16 + g * 8);
+          s = mfma(*(const bf16x8*)&Qs[buf][off], kf[ks], s);
+          dp = mfma(*(const bf16x8*)&Os[buf][off], vf[ks], dp);
+        }
+        // lane (g, j), value v = hh*8 + e: query row mb*32 + 16*hh + 8*g + e, key j
+        bf16x8 pb[2], db_[2];
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          const int rbase = mb * 32 + 16 * hh + 8 * g;
+          const f32x4 l0 = *(const f32x4*)&lse2s[buf][rbase], l1 = *(const f32x4*)&lse2s[buf][rbase + 4];
+          const f32x4 d0 = *(const f32x4*)&dels[buf][rbase], d1 = *(const f32x4*)&dels[buf][rbase + 4];
+          if (partial) {
+            asm volatile("" ::: "memory");   // keep this a real branch
+            const i32x4 p0 = *(const i32x4*)&qps[buf][rbase], p1 = *(const i32x4*)&qps[buf][rbase + 4];
+            const i32x4 q0 = *(const i32x4*)&qds[buf][rbase], q1 = *(const i32x4*)&qds[buf][rbase + 4];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              const int qp = e < 4 ? p0[e] : p1[e - 4];
+              const int qd = e < 4 ? q0[e] : q1[e - 4];
+              bool ok = true;
+              if (mask != MASK_NONE) ok = kpos <= qp;
+              if (mask == MASK_DOC_CAUSAL) ok = ok && kdoc == qd;
+              s[hh * 8 + e] = ok ? s[hh * 8 + e] : -INFINITY;
+            }
+          }
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const float l2 = e < 4 ? l0[e] : l1[e - 4];
+            const float de = e < 4 ? d0[e] : d1[e - 4];
+            const float p = fast_exp2(__builtin_fmaf(s[hh * 8 + e], sl2, -l2));
+            pb[hh][e] = (__bf16)p;
+            db_[hh][e] = (__bf16)(p * (dp[hh * 8 + e] - de));
+          }
+        }
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+          for (int db = 0; db < D / 32; ++db) {
+            dv[db] = mfma(pb[hh], tr_operand<D>(Os[buf], mb * 32 + 16 * hh, db * 32, lane), dv[db]);
+            dk[db] = mfma(db_[hh], tr_operand<D>(Qs[buf], mb * 32 + 16 * hh, db * 32, lane), dk[db]);
+          }
+      }
+      if (more) finish_tile(buf ^ 1);
+      __syncthreads();
+    }
+  }
+
+  // dk, dv += ; C layout: lane (g, j), value v -> key wave*32 + 8*(v/4) + 4*g + v%4, dim db*32 + j
+  const size_t obase = ((size_t)b * a.hkv + kvh) * a.sk;
+#pragma unroll
+  for (int v = 0; v < 16; ++v) {
+    const int kr_ = k0 + wave * 32 + 8 * (v / 4) + 4 * g + (v % 4);
+    if (kr_ >= a.sk) continue;
+    float* dkp = a.dk + (obase + kr_) * D;
+    float* dvp = a.dv + (obase + kr_) * D;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) {
+      dkp[db * 32 + j] += a.scale * dk[db][v];
+      dvp[db * 32 + j] += dv[db][v];
+    }
+  }
+}
+
+// ------------------------------------------------------------------ dQ
+template <int D>
+__global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
+  constexpr int CPW = BKT * D * 2 / 1024 / NWAVES;
+  __shared__ __attribute__((aligned(1024))) __bf16 Ks[2][BKT * D];
+  __shared__ __attribute__((aligned(1024))) __bf16 Vs[2][BKT * D];
+  __shared__ __attribute__((aligned(16))) int kvp[2][BKT];
+  __shared__ __attribute__((aligned(16))) int kvd[2][BKT];
+  __shared__ int list[LIST];
+  __shared__ int wave_cnt[NWAVES];
+
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, g = lane >> 5, j = lane & 31;
+  const int n_qt = (a.sq + BMQ - 1) / BMQ;
+  const int grp = a.hq / a.hkv;
+  int r = xcd_logical(blockIdx.x, n_qt * a.hq * a.B);
+  const int hh = r % grp; r /= grp;
+  const int qt = n_qt - 1 - (r % n_qt); r /= n_qt;
+  const int kvh = r % a.hkv, b = r / a.hkv;
+  const int h = kvh * grp + hh;
+  const int q0 = qt * BMQ;
+  const int mask = a.mask;
+
+  TileRange qr{0x7fffffff, (int)0x80000000, 0x7fffffff, (int)0x80000000};
+  for (int t = q0 / TILE; t < min(n_tiles(a.sq), (q0 + BMQ) / TILE); ++t) {
+    const TileRange x = a.q_tiles[t];
+    qr.min_pos = min(qr.min_pos, x.min_pos); qr.max_pos = max(qr.max_pos, x.max_pos);
+    qr.min_doc = min(qr.min_doc, x.min_doc); qr.max_doc = max(qr.max_doc, x.max_doc);
+  }
+
+  // this wave's 32 query rows: Q and dO as MFMA B operands (lane j = row)
+  const int qrow = q0 + wave * 32 + j;
+  const bool qvalid = qrow < a.sq;
+  const size_t qoff = b * a.qs.b + h * a.qs.h + (size_t)qrow * a.qs.s;
+  bf16x8 qf[D / 16], of[D / 16];
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks) {
+    bf16x8 z = {};
+    qf[ks] = qvalid ? *(const bf16x8*)((const __bf16*)a.q + qoff + ks * 16 + g * 8) : z;
+    of[ks] = qvalid ? *(const bf16x8*)((const __bf16*)a.d_o + qoff + ks * 16 + g * 8) : z;
+  }
+  const size_t lrow = ((size_t)b * a.hq + h) * a.sq + qrow;
+  float lse2 = INFINITY, delta = 0.f;
+  if (qvalid) {
+    const float l = a.lse[lrow];
+    lse2 = l == -INFINITY ? INFINITY : l * LOG2E;
+    delta = a.delta[lrow];
+  }
+  const int qpos = qvalid ? a.q_pos[qrow] : -1;
+  const int qdoc = (qvalid && mask == MASK_DOC_CAUSAL) ? a.q_doc[qrow] : 0;
+
+  f32x16 dq[D / 32];
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db) dq[db] = f32x16{};
+
+  const __bf16* kptr = (const __bf16*)a.k + b * a.kvs.b + kvh * a.kvs.h;
+  const __bf16* vptr = (const __bf16*)a.v + b * a.kvs.b + kvh * a.kvs.h;
+  const int rsb = (int)(a.kvs.s * 2);
+  const float sl2 = a.scale_log2;
+  int voff[CPW];
+#pragma unroll
+  for (int c = 0; c < CPW; ++c) voff[c] = chunk_voff<D>(c * NWAVES + wave, lane, rsb);
+  int preg = POS_INVALID, dreg = 0;
+
+  auto issue_tile = [&] __device__(int tile, int buf) {
+    const int kbase = tile * BKT;
+    const int rows = min(BKT, a.sk - kbase);
+#pragma unroll
+    for (int c = 0; c < CPW; ++c) {
+      const int q = c * NWAVES + wave;
+      dma16(kptr + (size_t)kbase * a.kvs.s, rows * rsb, (RA_LDS void*)&Ks[buf][q * 512], voff[c]);
+      dma16(vptr + (size_t)kbase * a.kvs.s, rows * rsb, (RA_LDS void*)&Vs[buf][q * 512], voff[c]);
+    }
+    if (tid < BKT) {
+      const int key = kbase + tid;
+      const bool ok = key < a.sk;
+      preg = ok ? a.kv_pos[key] : POS_INVALID;
+      dreg = (ok && mask == MASK_DOC_CAUSAL) ? a.kv_doc[key] : 0;
+    }
+  };
+  auto finish_tile = [&] __device__(int buf) {
+    if (tid < BKT) {
+      kvp[buf][tid] = preg;
+      kvd[buf][tid] = dreg;
+    }
+    wait_vmem();
+  };
+
+  const int nkt = n_tiles(a.sk);
+  const bool no_skip = (a.flags & FLAG_NO_SKIP) != 0;
+  for (int c0 = 0; c0 < nkt; c0 += LIST) {
+    const int total = build_list(c0, nkt, [&] __device__(int t) {
+      int c = classify(qr, a.kv_tiles[t], (t + 1) * TILE <= a.sk, mask);
+      return (no_skip && c == TILE_EMPTY) ? (int)TILE_PARTIAL : c;
+    }, list, wave_cnt);
+    if (total == 0) continue;
+    issue_tile(__builtin_amdgcn_readfirstlane(list[0]) & 0xffffff, 0);
+    finish_tile(0);
+    __syncthreads();
+
+    for (int li = 0; li < total; ++li) {
+      const int buf = li & 1;
+      const int ent = __builtin_amdgcn_readfirstlane(list[li]);
+      const bool partial = (ent >> 24) == TILE_PARTIAL;
+      const int kvalid = a.sk - (ent & 0xffffff) * BKT;
+      const bool more = li + 1 < total;
+      if (more) issue_tile(__builtin_amdgcn_readfirstlane(list[li + 1]) & 0xffffff, buf ^ 1);
+
+      f32x16 s[2], dp[2];
+      s[0] = s[1] = dp[0] = dp[1] = f32x16{};
+#pragma unroll
+      for (int ks = 0; ks < D / 16; ++ks)
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb) {
+          const int off = tile_off<D>(mb * 32 + swap23(j), ks * 16 + g * 8);
+          s[mb] = mfma(*(const bf16x8*)&Ks[buf][off], qf[ks], s[mb]);
+          dp[mb] = mfma(*(const bf16x8*)&Vs[buf][off], of[ks], dp[mb]);
+        }
+      // lane (g, j), value v = hh*8 + e of block mb: key mb*32 + 16*hh + 8*g + e, query j
+      if (partial) {
+        asm volatile("" ::: "memory");   // keep this a real branch
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+          for (int hh = 0; hh < 2; ++hh) {
+            const int base = mb * 32 + 16 * hh + 8 * g;
+            const i32x4 p0 = *(const i32x4*)&kvp[buf][base], p1 = *(const i32x4*)&kvp[buf][base + 4];
+            const i32x4 d0 = *(const i32x4*)&kvd[buf][base], d1 = *(const i32x4*)&kvd[buf][base + 4];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              const int kp = e < 4 ? p0[e] : p1[e - 4];
+              const int kd = e < 4 ? d0[e] : d1[e - 4];
+              bool ok = base + e < kvalid;
+              if (mask != MASK_NONE) ok = ok && kp <= qpos;
+              if (mask == MASK_DOC_CAUSAL) ok = ok && kd == qdoc;
+              s[mb][hh * 8 + e] = ok ? s[mb][hh * 8 + e] : -INFINITY;
+            }
+          }
+      }
+      bf16x8 dsb[4];
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int v = (kk & 1) * 8 + e;
+          const float p = fast_exp2(__builtin_fmaf(s[kk >> 1][v], sl2, -lse2));
+          dsb[kk][e] = (__bf16)(p * (dp[kk >> 1][v] - delta));
+        }
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) dq[db] = mfma(tr_operand<D>(Ks[buf], kk * 16, db * 32, lane), dsb[kk], dq[db]);
+      if (more) finish_tile(buf ^ 1);
+      __syncthreads();
+    }
+  }
+
+  if (!qvalid) return;
+  // dq += scale dQ; C layout of dQ^T: lane (g, j), value v -> dim db*32 + 8*(v/4) + 4*g + v%4, query j
+  float* dqp = a.dq + lrow * D;
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int vh = 0; vh < 4; ++vh) {
+      const int d = db * 32 + vh * 8 + g * 4;
+      f32x4 o = *(const f32x4*)(dqp + d);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) o[e] += a.scale * dq[db][vh * 4 + e];
+      *(f32x4*)(dqp + d) = o;
+    }
+}
+
+hipError_t launch_bwd_bf16(const BwdArgs& a, int d, hipStream_t st) {
+  const long dq_blocks = (long)((a.sq + BMQ - 1) / BMQ) * a.hq * a.B;
+  const long kv_blocks = (long)((a.sk + BK - 1) / BK) * a.hkv * a.B;
+  if (dq_blocks == 0 || kv_blocks == 0) return hipSuccess;
+  if (d == 128) {
+    bwd_dq_kernel<128><<<(unsigned)dq_blocks, 256, 0, st>>>(a);
+    bwd_dkdv_kernel<128><<<(unsigned)kv_blocks, 256, 0, st>>>(a);
+  } else {
+    bwd_dq_kernel<64><<<(unsigned)dq_blocks, 256, 0, st>>>(a);
+    bwd_dkdv_kernel<64><<<(unsigned)kv_blocks, 256, 0, st>>>(a);
+  }
+  return hipGetLastError();
+}
 
 }  // namespace ra

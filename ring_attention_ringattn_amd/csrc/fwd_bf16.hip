@@ -23,10 +23,9 @@
 // Data movement: K and V tiles go from HBM straight into LDS with buffer
 // loads (no register staging; the buffer range zero-fills keys past the end
 // of the block), double-buffered so the next tile streams in during the
-// current one's MFMAs; one barrier per tile.  Tiles are stored row-major with
-// the 16-byte units of each row XOR-swizzled by the row index, so both the
-// K operand reads (16 lanes, 16 different rows, one column) and the V
-// transpose reads (4 rows x 64 bytes per half-wave) hit distinct banks.
+// current one's MFMAs; one barrier per tile.  Tiles are row-major and
+// swizzled (mfma_tile.h) so the K operand reads and the V transpose reads
+// are free of bank conflicts.
 // Two workgroups fit on a CU, so one workgroup's softmax overlaps the other's
 // MFMAs.
 //
@@ -39,19 +38,9 @@
 // The step's normalised partial (O_t = acc / l, LSE_t = m ln2 + ln l) is
 // merged into the running (o_acc, lse) in the epilogue with the exact
 // log-sum-exp combine; FIRST overwrites, LAST also writes bf16 `out`.
-#include "ra_internal.h"
+#include "mfma_tile.h"
 
 namespace ra {
-
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef int i32x4 __attribute__((ext_vector_type(4)));
-
-#define RA_LDS __attribute__((address_space(3)))
 
 namespace {
 
@@ -59,63 +48,13 @@ constexpr int BN = 64;      // keys per tile (== TILE)
 constexpr int NWAVES = 4;
 constexpr int BM = NWAVES * 32;   // query rows per workgroup (32 per wave)
 constexpr int LIST = 256;   // tile-list chunk (one tile per thread when building it)
-constexpr float LN2 = 0.69314718055994530942f;
 constexpr float RESCALE_SLACK = 8.0f;
-constexpr int RSRC_WORD3 = 0x00020000;   // raw (untyped) buffer access on the gfx9 family
 
 template <int D>
 struct Cfg {
-  static constexpr int U = D / 8;                    // 16-byte units per row
   static constexpr int CHUNKS = BN * D * 2 / 1024;   // 1 KB buffer->LDS chunks per tile
   static constexpr int CPW = CHUNKS / NWAVES;        // ... per wave
 };
-
-__device__ __forceinline__ int swap23(int m) { return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1); }
-
-// Unit swizzles of the row-major tiles (see the file comment).
-template <int D>
-__device__ __forceinline__ int kswz(int r) { return D == 128 ? (r & 15) : ((r >> 1) & 7); }
-template <int D>
-__device__ __forceinline__ int vswz(int r) { return D == 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1); }
-
-__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
-
-// gfx950-only builtins live in device functions: used directly in a kernel
-// template body they make clang drop the kernel's host-side launch stub.
-
-// Copy 16 bytes per lane from base + voff into LDS at dst + 16*lane; bytes at
-// or past base + nbytes read as zero (buffer range check).
-__device__ __forceinline__ void dma16(const void* base, int nbytes, RA_LDS void* dst, int voff) {
-  const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, nbytes, RSRC_WORD3);
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, dst, 16, voff, 0, 0, 0);
-}
-
-// LDS transpose read of 4 bf16 (see the V operand comment in the kernel).
-__device__ __forceinline__ s16x4 lds_read_tr16(const __bf16* p) {
-  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((RA_LDS s16x4*)p);
-}
-
-
-// Both lanes of a (j, j+32) pair get the pair's maximum / sum.
-__device__ __forceinline__ float pair_max(float x) {
-  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-__device__ __forceinline__ float pair_sum(float x) {
-  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-
-// Merge weights of (lse_a) (+) (lse_b): returns lse, weights of a and b.
-__device__ __forceinline__ void lse_combine(float la, float lb, float& lse, float& wa, float& wb) {
-  const float mx = fmaxf(la, lb);
-  if (mx == -INFINITY) { lse = -INFINITY; wa = 0.f; wb = 0.f; return; }
-  const float ea = expf(la - mx), eb = expf(lb - mx);
-  const float s = ea + eb;
-  lse = mx + logf(s);
-  wa = ea / s;
-  wb = eb / s;
-}
 
 // Workgroup -> (batch, query head, query tile).  Hardware hands consecutive
 // workgroup ids to the 8 XCDs round-robin; renumber so that each XCD gets a
@@ -124,12 +63,8 @@ __device__ __forceinline__ void lse_combine(float la, float lb, float& lse, floa
 // stream the same K/V tiles at about the same time, and the query tiles that
 // see the most keys under a causal mask start first.
 __device__ __forceinline__ void map_block(int n_qt, int hq, int hkv, int total, int& b, int& h, int& qt) {
-  const int i = blockIdx.x;
-  const int per = total / 8, rem = total % 8;
-  const int xcd = i % 8, local = i / 8;
-  const int logical = xcd < rem ? xcd * (per + 1) + local : rem * (per + 1) + (xcd - rem) * per + local;
   const int grp = hq / hkv;
-  int r = logical;
+  int r = xcd_logical(blockIdx.x, total);
   const int hh = r % grp; r /= grp;
   qt = n_qt - 1 - (r % n_qt); r /= n_qt;
   const int kvh = r % hkv;
@@ -196,14 +131,9 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs a) {
   // Per-lane byte offsets (within a tile) of this lane's 16-byte unit of each
   // of the wave's CPW buffer->LDS chunks: chunk q = c*4 + wave covers LDS
   // units [64q, 64q+64); unit p holds row p/U, logical column (p%U) ^ swz(row).
-  int voff_k[C::CPW], voff_v[C::CPW];
+  int voff[C::CPW];
 #pragma unroll
-  for (int c = 0; c < C::CPW; ++c) {
-    const int p = (c * NWAVES + wave) * 64 + lane;
-    const int r = p / C::U, pu = p % C::U;
-    voff_k[c] = r * rsb + (pu ^ kswz<D>(r)) * 16;
-    voff_v[c] = r * rsb + (pu ^ vswz<D>(r)) * 16;
-  }
+  for (int c = 0; c < C::CPW; ++c) voff[c] = chunk_voff<D>(c * NWAVES + wave, lane, rsb);
   int preg = POS_INVALID, dreg = 0;
 
   // Start streaming tile `tile` into LDS buffer `buf`.
@@ -215,8 +145,8 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs a) {
 #pragma unroll
     for (int c = 0; c < C::CPW; ++c) {
       const int q = c * NWAVES + wave;
-      dma16(kb, rows * rsb, (RA_LDS void*)&Ks[buf][q * 512], voff_k[c]);
-      dma16(vb, rows * rsb, (RA_LDS void*)&Vs[buf][q * 512], voff_v[c]);
+      dma16(kb, rows * rsb, (RA_LDS void*)&Ks[buf][q * 512], voff[c]);
+      dma16(vb, rows * rsb, (RA_LDS void*)&Vs[buf][q * 512], voff[c]);
     }
     if (tid < BN) {
       const int key = kbase + tid;
@@ -230,7 +160,7 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs a) {
       kvp[buf][tid] = preg;
       kvd[buf][tid] = dreg;
     }
-    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this thread's buffer->LDS loads have landed
+    wait_vmem();   // this thread's buffer->LDS loads have landed
   };
 
   for (int c0 = 0; c0 < nkt; c0 += LIST) {
@@ -277,9 +207,8 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs a) {
       for (int ks = 0; ks < D / 16; ++ks) {
 #pragma unroll
         for (int mb = 0; mb < 2; ++mb) {
-          const int r = mb * 32 + swap23(j);
-          const bf16x8 kf = *(const bf16x8*)(&Ks[buf][r * D + (((ks * 2 + g) ^ kswz<D>(r)) * 8)]);
-          s[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], s[mb], 0, 0, 0);
+          const bf16x8 kf = *(const bf16x8*)(&Ks[buf][tile_off<D>(mb * 32 + swap23(j), ks * 16 + g * 8)]);
+          s[mb] = mfma(kf, qf[ks], s[mb]);
         }
       }
 
@@ -337,25 +266,10 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs a) {
       l_run += rs;
 
       // ---- O^T += V^T P^T, V^T from the row-major tile by transpose reads ----
-      // 16-lane group G of lane l: source lane s = l%16 points at key
-      // kk*16 + (G/2)*8 + half*4 + s/4, dims db*32 + (G%2)*16 + 4*(s%4) .. +3.
-      const int G = lane >> 4, sl = lane & 15;
 #pragma unroll
-      for (int db = 0; db < D / 32; ++db) {
-        const int dcol = db * 32 + (G & 1) * 16 + 4 * (sl & 3);
+      for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-          s16x4 half[2];
-#pragma unroll
-          for (int hf = 0; hf < 2; ++hf) {
-            const int key = kk * 16 + (G >> 1) * 8 + hf * 4 + (sl >> 2);
-            const int off = key * D + (((dcol >> 3) ^ vswz<D>(key)) << 3) + (dcol & 7);
-            half[hf] = lds_read_tr16(&Vs[buf][off]);
-          }
-          const bf16x8 vf = __builtin_bit_cast(bf16x8, __builtin_shufflevector(half[0], half[1], 0, 1, 2, 3, 4, 5, 6, 7));
-          acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[kk], acc[db], 0, 0, 0);
-        }
-      }
+        for (int kk = 0; kk < 4; ++kk) acc[db] = mfma(tr_operand<D>(Vs[buf], kk * 16, db * 32, lane), pf[kk], acc[db]);
       if (more) finish_tile(buf ^ 1);
       __syncthreads();
     }
@@ -366,7 +280,7 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs a) {
   const bool last = (a.flags & FLAG_LAST) != 0 && a.out != nullptr;
   const float l_tot = pair_sum(l_run);
   if (!qvalid) return;
-  const float lse_t = l_tot > 0.f ? (m_run + log2f(l_tot)) * LN2 : -INFINITY;
+  const float lse_t = l_tot > 0.f ? (m_run + log2f(l_tot)) * LN2F : -INFINITY;
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
   const size_t orow = ((size_t)b * a.hq + h) * a.sq + qrow;
   float lse_new = lse_t, w_p = 0.f, w_t = inv;

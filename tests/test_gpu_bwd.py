@@ -1,0 +1,157 @@
+"""Backward parity on the GPU: ringattn_run(pass=backward) against the fp64 oracle.
+
+Tolerance: dQ, dK, dV relative L2 error <= 2e-2 (bf16 inputs).  dK/dV of a
+block collect the contributions of the emulated ranks' queries only, which is
+what the oracle computes when given just those query rows.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import ring_attention_ringattn_amd as ra
+import synthetic
+from tests.gpu_util import Ring, dev, max_abs, print_case, rel_l2
+
+pytestmark = pytest.mark.gpu
+
+TOL = 2e-2
+
+
+def _global_grads(inp, rows, mask, doc=None):
+    """Oracle dQ (for `rows`) and dK, dV (contributions of `rows`) over the whole context."""
+    s = inp["k"].shape[2]
+    where = {int(g): i for i, g in enumerate(inp["q_rows"])}
+    sel = [where[int(g)] for g in rows]
+    return oracle.attention_backward(inp["q"][:, :, sel], inp["k"], inp["v"], inp["do"][:, :, sel], rows,
+                                     np.arange(s), mask, None if doc is None else doc[rows], doc,
+                                     row_block=128, skip_masked_columns=mask != "none")
+
+
+def _check(ring, inp, mask, doc=None, rows_per_rank=None):
+    rows = np.concatenate([ring.pos[r] for r in ring.ranks])
+    dQ, dK, dV = _global_grads(inp, rows, mask, doc)
+    off = 0
+    for i, r in enumerate(ring.ranks):
+        n = ring.pos[r].size
+        e = rel_l2(ring.numpy("dq")[i], dQ[:, :, off:off + n])
+        print(f"  rank {r}: dQ rel L2 {e:.3g}", flush=True)
+        assert e <= TOL
+        off += n
+    for n_, p in enumerate(ring.pos):
+        ek = rel_l2(ring.numpy("dk")[n_], dK[:, :, p])
+        ev = rel_l2(ring.numpy("dv")[n_], dV[:, :, p])
+        print(f"  block {n_}: dK rel L2 {ek:.3g} dV rel L2 {ev:.3g}", flush=True)
+        assert ek <= TOL and ev <= TOL
+
+
+def test_bwd_zigzag_ring_all_ranks():
+    print_case("bwd: zigzag 4 ranks, 2048 tokens, 8/2 GQA heads, D=128, all ranks")
+    w = synthetic.small_workload("c4", seq=2048, n_shards=4, hq=8, hkv=2, seed=41)
+    inp = synthetic.make_inputs(w)
+    pos = ra.sharding.shard_positions(w.seq, 4, "zigzag")
+    ring = Ring(inp["q"], inp["k"], inp["v"], pos, "causal", "bf16", range(4), do_glob=inp["do"])
+    ring.forward().backward()
+    _check(ring, inp, "causal")
+
+
+def test_bwd_rank_share_medium():
+    """The launch configuration of the 262144-token share, scaled to 16384 tokens: rank 0 of 8, 32/8 heads."""
+    print_case("bwd: rank 0 of 8 zigzag shards, 16384 tokens, 32/8 GQA heads, D=128")
+    w = synthetic.small_workload("c4", seq=16384, seed=42)
+    pos = ra.sharding.shard_positions(w.seq, 8, "zigzag")
+    inp = synthetic.make_inputs(w, q_rows=pos[0])
+    ring = Ring(None, inp["k"], inp["v"], pos, "causal", "bf16", [0], q_shards=[inp["q"]], do_shards=[inp["do"]])
+    ring.forward().backward()
+    _check(ring, inp, "causal")
+
+
+def test_bwd_doc_causal_thd_all_ranks():
+    print_case("bwd: packed documents, THD layout, 4 contiguous shards of 8192 tokens, 8/2 heads")
+    w = synthetic.small_workload("c5", seq=8192, n_shards=4, hq=8, hkv=2, seed=43)
+    inp = synthetic.make_inputs(w)
+    lens = synthetic.doc_lengths(43, 8192, median=600.0)
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    doc = oracle.docs_from_cu_seqlens(cu, 8192)
+    pos = ra.sharding.shard_positions(8192, 4, "contiguous")
+    ring = Ring(inp["q"], inp["k"], inp["v"], pos, "doc_causal", "bf16", range(4), doc=doc, layout="thd",
+                do_glob=inp["do"])
+    ring.forward().backward()
+    _check(ring, inp, "doc_causal", doc)
+
+
+@pytest.mark.parametrize("case", [("none", 64, 130, 200), ("causal", 64, 257, 190), ("causal", 128, 100, 333)],
+                         ids=lambda c: "-".join(map(str, c)))
+def test_step_bwd_ragged(case):
+    """One backward step on ragged sizes with scattered positions (step entry point, D=64 and 128)."""
+    mask, d, sq, sk = case
+    print_case(f"step_bwd {case}")
+    rng = np.random.default_rng(sq * 1000 + sk)
+    rnd = lambda *s: synthetic.bf16_round(0.5 * rng.standard_normal(s).astype(np.float32))
+    B, hq, hkv = 2, 4, 2
+    q, k, v, do = rnd(B, hq, sq, d), rnd(B, hkv, sk, d), rnd(B, hkv, sk, d), rnd(B, hq, sq, d)
+    perm = rng.permutation(sq + sk).astype(np.int32)
+    qp, kp = perm[:sq], perm[sq:]
+    if mask == "causal":
+        qp = np.maximum(qp, 5).astype(np.int32)     # every query sees at least one key below it
+        kp[0] = 0
+    O, L = oracle.attention_forward(q, k, v, qp, kp, mask)
+    dQ, dK, dV = oracle.attention_backward(q, k, v, do, qp, kp, mask)
+    bf = torch.bfloat16
+    out = dev(O, bf)
+    delta = torch.zeros(B, hq, sq, device="cuda")
+    ra.ringattn_bwd_preprocess(out, dev(do, bf), delta)
+    dq = torch.zeros(B, hq, sq, d, device="cuda")
+    dk = torch.zeros(B, hkv, sk, d, device="cuda")
+    dv = torch.zeros(B, hkv, sk, d, device="cuda")
+    ra.ringattn_step_bwd(dev(q, bf), dev(k, bf), dev(v, bf), dev(do, bf), dev(L), delta, dq, dk, dv,
+                         dev(qp, torch.int32), dev(kp, torch.int32),
+                         mask_mode={"none": ra.RA_MASK_NONE, "causal": ra.RA_MASK_CAUSAL}[mask])
+    torch.cuda.synchronize()
+    ref_delta = np.sum(do.astype(np.float64) * out.float().cpu().numpy(), axis=-1)
+    assert max_abs(delta.cpu().numpy(), ref_delta) <= 1e-4
+    for got, ref, name in ((dq, dQ, "dQ"), (dk, dK, "dK"), (dv, dV, "dV")):
+        e = rel_l2(got.cpu().numpy(), ref)
+        print(f"  {name} rel L2 {e:.3g}", flush=True)
+        assert e <= TOL
+
+
+def test_bwd_full_size_rank_share():
+    """262144-token context, rank 0 of 8 (32768 queries, 8 blocks of 32768 keys), forward + backward.
+
+    Exact per sampled row: O, LSE and dQ.  For dK/dV the identities that hold
+    at any size: summed over every key of every block, dK vanishes (each row's
+    dS sums to zero) and dV equals the sum of the rank's dO rows over the GQA
+    group (each row's weights sum to one).
+    """
+    w = synthetic.WORKLOADS["c4"]
+    print_case("c4: bf16 rank 0 of 8, 32768 local queries, 8 steps of 32768 keys, forward + backward")
+    pos = ra.sharding.shard_positions(w.seq, w.n_shards, w.sharding)
+    inp = synthetic.make_inputs(w, q_rows=pos[0])
+    ring = Ring(None, inp["k"], inp["v"], pos, "causal", "bf16", [0], q_shards=[inp["q"]], do_shards=[inp["do"]])
+    ring.forward().backward()
+    rng = np.random.default_rng(7)
+    c = w.seq // (2 * w.n_shards)
+    local = np.unique(np.concatenate([rng.choice(pos[0].size, 24, replace=False), [0, c - 1, c, 2 * c - 1]]))
+    rows = pos[0][local]
+    O, L = oracle.attention_forward(inp["q"][:, :, local], inp["k"], inp["v"], rows, np.arange(w.seq), "causal",
+                                    row_block=128, skip_masked_columns=True)
+    assert max_abs(ring.numpy("out")[0][:, :, local], O) <= 1e-2
+    assert max_abs(ring.numpy("lse")[0][:, :, local], L) <= 1e-3
+    dQ, _, _ = oracle.attention_backward(inp["q"][:, :, local], inp["k"], inp["v"], inp["do"][:, :, local], rows,
+                                         np.arange(w.seq), "causal", row_block=128, skip_masked_columns=True)
+    e = rel_l2(ring.numpy("dq")[0][:, :, local], dQ)
+    print(f"  sampled dQ rows rel L2 {e:.3g}", flush=True)
+    assert e <= TOL
+    dk_sum = sum(t.double().sum(dim=2) for t in ring.dk)           # [B, Hkv, D]
+    dk_norm = torch.sqrt(sum((t.double() ** 2).sum(dim=2) for t in ring.dk))
+    ratio = float((dk_sum.norm() / dk_norm.norm()).item())
+    print(f"  |sum_j dK_j| / sqrt(sum_j |dK_j|^2) = {ratio:.3g}", flush=True)
+    assert ratio <= 5e-2
+    dv_sum = sum(t.double().sum(dim=2) for t in ring.dv).cpu().numpy()
+    do_sum = inp["do"].astype(np.float64).reshape(1, w.hkv, w.hq // w.hkv, -1, w.head_dim).sum(axis=(2, 3))
+    e = rel_l2(dv_sum, do_sum)
+    print(f"  sum_j dV_j vs group sum of dO: rel L2 {e:.3g}", flush=True)
+    assert e <= TOL
+    for t in ring.dq + ring.dk + ring.dv:
+        assert torch.isfinite(t).all()
