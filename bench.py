@@ -31,17 +31,66 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA: 256 CUs x 4096 FLOP/clk x 2.4 GHz
 PEAK_HBM_GBS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fwd_bf16_c3_traffic.json")
+KERNEL_SOURCES = ("ring_attention_ringattn_amd/csrc/fwd_bf16.hip", "ring_attention_ringattn_amd/csrc/mfma_tile.h",
+                  "ring_attention_ringattn_amd/csrc/ra_internal.h")
+
+
+def kernel_source_hash():
+    """sha256 over the sources of the forward step kernel (to tell whether counters are stale)."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        h.update(open(os.path.join(ROOT, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per launch of the forward step kernel from the committed counter summary, or None
+    when that summary is missing or was taken on other kernel sources."""
+    try:
+        t = json.load(open(TRAFFIC_FILE))
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_source_sha256") != kernel_source_hash():
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def copy_calibration():
+    """A plain device copy of known size, for scaling the FETCH_SIZE / WRITE_SIZE counters."""
+    import torch
+    n = 64 * 1024 * 1024
+    x = torch.empty(n, dtype=torch.float32, device="cuda").fill_(1.0)
+    y = torch.empty_like(x)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        y.copy_(x)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes_read_per_copy": n * 4, "bytes_written_per_copy": n * 4,
+                      "copies": 3}), flush=True)
 METRIC = "causal-effective attention TFLOP/s per rank-share (fwd, fwd+bwd); % bf16 MFMA peak"
 
 
-def visible_pairs(q_pos, kv_pos):
-    """Causal visible (query, key) pairs: sum over queries of keys with kv_pos <= q_pos."""
+def visible_pairs(q_pos, kv_pos, docs=None):
+    """Visible (query, key) pairs: keys with kv_pos <= q_pos (and, with documents, in the query's document)."""
     import numpy as np
-    ks = np.sort(np.asarray(kv_pos, dtype=np.int64))
-    return int(np.searchsorted(ks, np.asarray(q_pos, dtype=np.int64), side="right").sum())
+    q_pos = np.asarray(q_pos, dtype=np.int64)
+    kv_pos = np.asarray(kv_pos, dtype=np.int64)
+    if docs is None:
+        ks = np.sort(kv_pos)
+        return int(np.searchsorted(ks, q_pos, side="right").sum())
+    # documents are contiguous position ranges: count per query the keys in [doc start, q_pos]
+    starts = np.zeros(docs.max() + 2, dtype=np.int64)
+    starts[1:] = np.cumsum(np.bincount(docs))
+    ks = np.sort(kv_pos)
+    lo = np.searchsorted(ks, starts[docs[q_pos]], side="left")
+    hi = np.searchsorted(ks, q_pos, side="right")
+    return int(np.maximum(hi - lo, 0).sum())
 
 
-def setup_share(wname, rank, with_bwd):
+def setup_share(wname, ranks, with_bwd):
+    """Device tensors of a ring: the listed (consecutive) ranks' query shards and all N home blocks."""
     import numpy as np
     import torch
 
@@ -51,32 +100,53 @@ def setup_share(wname, rank, with_bwd):
     w = synthetic.WORKLOADS[wname]
     n = w.n_shards
     pos = ra.sharding.shard_positions(w.seq, n, w.sharding)
-    inp = synthetic.make_inputs(w, q_rows=pos[rank], backward=with_bwd)
+    q_rows = np.concatenate([pos[r] for r in ranks])
+    inp = synthetic.make_inputs(w, q_rows=q_rows, backward=with_bwd)
     bf = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda().to(torch.bfloat16)
+    sl = lambda arr, i: arr[:, :, i * pos[0].size:(i + 1) * pos[0].size]
     s = {
-        "w": w, "n": n, "rank": rank, "pos": pos, "inp": inp,
-        "q": [bf(inp["q"])],
+        "w": w, "n": n, "ranks": list(ranks), "pos": pos, "inp": inp,
+        "q": [bf(sl(inp["q"], i)) for i in range(len(ranks))],
         "k": [bf(inp["k"][:, :, p]) for p in pos],
         "v": [bf(inp["v"][:, :, p]) for p in pos],
-        "q_pos": [torch.from_numpy(pos[rank]).cuda()],
+        "q_pos": [torch.from_numpy(pos[r]).cuda() for r in ranks],
         "kv_pos": [torch.from_numpy(p).cuda() for p in pos],
+        "q_doc": None, "kv_doc": None,
+        "mask": ra.RA_MASK_DOC_CAUSAL if w.mask == "doc_causal" else ra.RA_MASK_CAUSAL,
     }
+    if inp["cu_seqlens"] is not None:
+        cu = torch.from_numpy(inp["cu_seqlens"]).cuda()
+        s["kv_doc"] = [ra.ringattn_docs_from_cu_seqlens(cu, int(p[0]), p.size) for p in pos]
+        s["q_doc"] = [s["kv_doc"][r] for r in ranks]
     if with_bwd:
-        s["do"] = [bf(inp["do"])]
+        s["do"] = [bf(sl(inp["do"], i)) for i in range(len(ranks))]
     shp = s["q"][0].shape
-    s["o_acc"] = [torch.empty(shp, dtype=torch.float32, device="cuda")]
-    s["lse"] = [torch.empty(shp[:3], dtype=torch.float32, device="cuda")]
-    s["out"] = [torch.empty(shp, dtype=torch.bfloat16, device="cuda")]
-    s["pairs_per_step"] = [visible_pairs(pos[rank], pos[ra.sharding.block_of(rank, t, n)]) for t in range(n)]
-    s["ws"] = torch.empty(ra.ringattn_run_workspace_size(s["q"][0], s["k"][0], n, 1), dtype=torch.uint8,
-                          device="cuda")
+    s["o_acc"] = [torch.empty(shp, dtype=torch.float32, device="cuda") for _ in ranks]
+    s["lse"] = [torch.empty(shp[:3], dtype=torch.float32, device="cuda") for _ in ranks]
+    s["out"] = [torch.empty(shp, dtype=torch.bfloat16, device="cuda") for _ in ranks]
+    docs = None
+    if inp["cu_seqlens"] is not None:
+        cu_np = inp["cu_seqlens"]
+        docs = np.searchsorted(cu_np, np.arange(w.seq), side="right") - 1
+    s["pairs_per_step"] = [sum(visible_pairs(pos[r], pos[ra.sharding.block_of(r, t, n)], docs) for r in ranks)
+                           for t in range(n)]
+    s["ws"] = torch.empty(ra.ringattn_run_workspace_size(s["q"][0], s["k"][0], n, len(ranks),
+                                                         pass_=ra.RA_PASS_BWD if with_bwd else ra.RA_PASS_FWD),
+                          dtype=torch.uint8, device="cuda")
+    if with_bwd:
+        kshp = s["k"][0].shape
+        s["delta"] = [torch.empty(shp[:3], dtype=torch.float32, device="cuda") for _ in ranks]
+        s["dq"] = [torch.empty(shp, dtype=torch.float32, device="cuda") for _ in ranks]
+        s["dk"] = [torch.empty(kshp, dtype=torch.float32, device="cuda") for _ in range(n)]
+        s["dv"] = [torch.empty(kshp, dtype=torch.float32, device="cuda") for _ in range(n)]
     return s
 
 
 def run_fwd(s, side, events=None):
     import ring_attention_ringattn_amd as ra
     ra.ringattn_run(s["q"], s["k"], s["v"], s["q_pos"], s["kv_pos"], o_acc=s["o_acc"], lse=s["lse"], out=s["out"],
-                    first_rank=s["rank"], workspace=s["ws"], copy_stream=side, step_events=events)
+                    q_doc=s["q_doc"], kv_doc=s["kv_doc"], first_rank=s["ranks"][0], mask_mode=s["mask"],
+                    workspace=s["ws"], copy_stream=side, step_events=events)
 
 
 def run_bwd(s, side):
@@ -84,8 +154,26 @@ def run_bwd(s, side):
     for t in s["dq"] + s["dk"] + s["dv"]:
         t.zero_()
     ra.ringattn_run(s["q"], s["k"], s["v"], s["q_pos"], s["kv_pos"], lse=s["lse"], out=s["out"], d_o=s["do"],
-                    delta=s["delta"], dq=s["dq"], dk=s["dk"], dv=s["dv"], first_rank=s["rank"],
-                    pass_=ra.RA_PASS_BWD, workspace=s["ws"], copy_stream=side)
+                    q_doc=s["q_doc"], kv_doc=s["kv_doc"], delta=s["delta"], dq=s["dq"], dk=s["dk"], dv=s["dv"],
+                    first_rank=s["ranks"][0], mask_mode=s["mask"], pass_=ra.RA_PASS_BWD, workspace=s["ws"],
+                    copy_stream=side)
+
+
+def fwd_bwd_leg(name, ranks, side, steps, warmup, label):
+    import torch
+    s = setup_share(name, ranks, with_bwd=True)
+    w = s["w"]
+    p = sum(s["pairs_per_step"])
+    t_f = timed(lambda: run_fwd(s, side), steps, warmup)
+    t_b = timed(lambda: run_bwd(s, side), steps, warmup)
+    fl_f, fl_b = 4.0 * w.head_dim * w.hq * w.batch * p, 10.0 * w.head_dim * w.hq * w.batch * p
+    del s
+    torch.cuda.empty_cache()
+    return {"workload": label, "visible_pairs_per_head": p,
+            "fwd_ms": round(t_f * 1e3, 3), "bwd_ms": round(t_b * 1e3, 3),
+            "fwd_tflops": round(fl_f / t_f / 1e12, 2), "bwd_tflops": round(fl_b / t_b / 1e12, 2),
+            "fwd_bwd_tflops": round((fl_f + fl_b) / (t_f + t_b) / 1e12, 2),
+            "fwd_bwd_pct_peak": round(100.0 * (fl_f + fl_b) / (t_f + t_b) / 1e12 / PEAK_BF16_TFLOPS, 2)}
 
 
 def timed(fn, steps, warmup):
@@ -137,20 +225,26 @@ def main():
     ap.add_argument("--steps", type=int, default=9, help="timed rings (the pages' method: 10 runs, first dropped)")
     ap.add_argument("--warmup", type=int, default=1)
     ap.add_argument("--rank", type=int, default=0)
-    ap.add_argument("--bwd", action="store_true", help="also time forward+backward of the 262144-token share")
+    ap.add_argument("--no-bwd", action="store_true", help="skip the forward+backward legs")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for the CPU baseline")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 256 MiB device copy (for scaling HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU's share of the ring; --gpus {args.gpus} is not supported "
               "(this build runs on a single MI355X and emulates the ring's ranks on it)", file=sys.stderr)
         sys.exit(2)
 
+    if args.copy_calibration:
+        copy_calibration()
+        return
+
     import torch
     import ring_attention_ringattn_amd as ra
 
     torch.cuda.set_device(0)
-    s = setup_share("c3", args.rank, with_bwd=False)
+    s = setup_share("c3", [args.rank], with_bwd=False)
     side = torch.cuda.Stream()
     n = s["n"]
     w = s["w"]
@@ -196,33 +290,25 @@ def main():
                    "ring_steps": n, "parallelism": "cp8 (ring emulated on one GPU)"},
         "pct_peak": round(100.0 * flops_ring / t_ring / 1e12 / PEAK_BF16_TFLOPS, 2),
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": measured_traffic(),
                      "kernel": "ra::fwd_bf16_kernel<128,*>",
                      "per_launch_ms": [round(x, 4) for x in kern_ms],
                      "flop_per_launch": flops_step},
     }
 
-    if args.bwd:
+    if not args.no_bwd:
         del s
         torch.cuda.empty_cache()
-        b = setup_share("c4", args.rank, with_bwd=True)
-        shp, kshp = b["q"][0].shape, b["k"][0].shape
-        b["delta"] = [torch.empty(shp[:3], dtype=torch.float32, device="cuda")]
-        b["dq"] = [torch.empty(shp, dtype=torch.float32, device="cuda")]
-        b["dk"] = [torch.empty(kshp, dtype=torch.float32, device="cuda") for _ in range(b["n"])]
-        b["dv"] = [torch.empty(kshp, dtype=torch.float32, device="cuda") for _ in range(b["n"])]
-        b["ws"] = torch.empty(ra.ringattn_run_workspace_size(b["q"][0], b["k"][0], b["n"], 1, pass_=ra.RA_PASS_BWD),
-                              dtype=torch.uint8, device="cuda")
-        p = sum(b["pairs_per_step"])
-        wb = b["w"]
-        t_f = timed(lambda: run_fwd(b, side), args.steps, args.warmup)
-        t_b = timed(lambda: run_bwd(b, side), args.steps, args.warmup)
-        fl_f, fl_b = 4.0 * wb.head_dim * wb.hq * p, 10.0 * wb.head_dim * wb.hq * p
-        result["fwd_bwd"] = {"workload": "rank share of a 262144-token causal context over 8 zigzag shards "
-                                         "(32768 local queries, 8 steps of 32768-token blocks), bf16",
-                             "fwd_ms": round(t_f * 1e3, 3), "bwd_ms": round(t_b * 1e3, 3),
-                             "fwd_tflops": round(fl_f / t_f / 1e12, 2), "bwd_tflops": round(fl_b / t_b / 1e12, 2),
-                             "fwd_bwd_tflops": round((fl_f + fl_b) / (t_f + t_b) / 1e12, 2)}
+        result["legs"] = {
+            "fwd_bwd_262144_rank_share": fwd_bwd_leg(
+                "c4", [args.rank], side, args.steps, args.warmup,
+                "rank share of a 262144-token causal context over 8 zigzag shards (32768 local queries, "
+                "8 steps of 32768-token blocks), 32/8 heads, D=128, bf16, forward + backward"),
+            "fwd_bwd_packed_documents": fwd_bwd_leg(
+                "c5", [0, 1, 2, 3], side, args.steps, args.warmup,
+                "65536 packed tokens of lognormal documents (seed 5: 22 documents), document-causal, "
+                "4 contiguous ring shards, all ranks, 32/8 heads, D=128, bf16, forward + backward"),
+        }
 
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(*host, args.cpu_budget)

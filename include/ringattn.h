@@ -89,7 +89,9 @@ enum {
 enum {
   RA_RUN_SERIAL_COPY = 16,   /* copy each block on the compute stream (no overlap) */
   RA_RUN_POISON = 32,        /* fill a staging slot with NaN right before each copy into it */
-  RA_RUN_MERGE_KERNEL = 64   /* forward: step kernel writes a separate partial, then ringattn_merge */
+  RA_RUN_MERGE_KERNEL = 64,  /* forward: step kernel writes a separate partial, then ringattn_merge */
+  RA_RUN_COPY_ENGINE = 128   /* stage blocks with the DMA-engine copy (hipMemcpyDeviceToDeviceNoCU)
+                                instead of a copy kernel that shares the compute units */
 };
 
 enum { RA_PASS_FWD = 1, RA_PASS_BWD = 2 };

@@ -21,15 +21,16 @@ import torch
 
 from . import _lib
 from ._lib import (RA_BF16, RA_F32, RA_MASK_CAUSAL, RA_MASK_DOC_CAUSAL, RA_MASK_NONE, RA_MAX_SK, RA_NO_SKIP,
-                   RA_PASS_BWD, RA_PASS_FWD, RA_RUN_MERGE_KERNEL, RA_RUN_POISON, RA_RUN_SERIAL_COPY, RA_STEP_FIRST,
-                   RA_STEP_LAST, RingAttnError)
+                   RA_PASS_BWD, RA_PASS_FWD, RA_RUN_COPY_ENGINE, RA_RUN_MERGE_KERNEL, RA_RUN_POISON,
+                   RA_RUN_SERIAL_COPY, RA_STEP_FIRST, RA_STEP_LAST, RingAttnError)
 from . import sharding
 
 __all__ = ["ringattn_step_workspace_size", "ringattn_step_fwd", "ringattn_merge", "ringattn_bwd_preprocess",
            "ringattn_step_bwd", "ringattn_run_workspace_size", "ringattn_run", "ringattn_docs_from_cu_seqlens",
            "ringattn_last_error", "ringattn_version", "make_problem", "RingAttnError", "sharding",
            "RA_MASK_NONE", "RA_MASK_CAUSAL", "RA_MASK_DOC_CAUSAL", "RA_STEP_FIRST", "RA_STEP_LAST", "RA_NO_SKIP",
-           "RA_RUN_SERIAL_COPY", "RA_RUN_POISON", "RA_RUN_MERGE_KERNEL", "RA_PASS_FWD", "RA_PASS_BWD",
+           "RA_RUN_SERIAL_COPY", "RA_RUN_POISON", "RA_RUN_MERGE_KERNEL", "RA_RUN_COPY_ENGINE", "RA_PASS_FWD",
+           "RA_PASS_BWD",
            "RA_F32", "RA_BF16", "RA_MAX_SK"]
 
 _DTYPES = {torch.float32: RA_F32, torch.bfloat16: RA_BF16}

@@ -16,7 +16,7 @@ RA_OK, RA_ERR_INVALID, RA_ERR_UNSUPPORTED, RA_ERR_WORKSPACE, RA_ERR_HIP = 0, -1,
 RA_MASK_NONE, RA_MASK_CAUSAL, RA_MASK_DOC_CAUSAL = 0, 1, 2
 RA_F32, RA_BF16 = 0, 1
 RA_STEP_FIRST, RA_STEP_LAST, RA_NO_SKIP = 1, 2, 4
-RA_RUN_SERIAL_COPY, RA_RUN_POISON, RA_RUN_MERGE_KERNEL = 16, 32, 64
+RA_RUN_SERIAL_COPY, RA_RUN_POISON, RA_RUN_MERGE_KERNEL, RA_RUN_COPY_ENGINE = 16, 32, 64, 128
 RA_PASS_FWD, RA_PASS_BWD = 1, 2
 RA_MAX_SK = 262144
 

@@ -331,7 +331,7 @@ RunLayout run_layout(const ra_run_desc* d) {
   return L;
 }
 
-const int kRunFlags = RA_NO_SKIP | RA_RUN_SERIAL_COPY | RA_RUN_POISON | RA_RUN_MERGE_KERNEL;
+const int kRunFlags = RA_NO_SKIP | RA_RUN_SERIAL_COPY | RA_RUN_POISON | RA_RUN_MERGE_KERNEL | RA_RUN_COPY_ENGINE;
 
 int check_run(const ra_run_desc* d) {
   if (!d) return fail(RA_ERR_INVALID, "run descriptor is NULL");
@@ -455,6 +455,8 @@ extern "C" int ringattn_run(const ra_run_desc* d, const void* const* q, const vo
   const bool serial = (d->flags & RA_RUN_SERIAL_COPY) || xs == nullptr || xs == cs;
   if (serial) xs = cs;
   const bool poison = (d->flags & RA_RUN_POISON) != 0;
+  const hipMemcpyKind copy_kind = (d->flags & RA_RUN_COPY_ENGINE) ? hipMemcpyDeviceToDeviceNoCU
+                                                                    : hipMemcpyDeviceToDevice;
   const int step_flags_extra = d->flags & RA_NO_SKIP;
   char* ws = (char*)workspace;
   auto slot_k = [&](int slot, int i) { return (void*)(ws + L.off_slots + ((size_t)(slot * R + i) * 2 + 0) * L.blk_bytes); };
@@ -506,10 +508,8 @@ extern "C" int ringattn_run(const ra_run_desc* d, const void* const* q, const vo
         if ((err = launch_fill_nan(slot_k(slot, i), copy_bytes, xs)) != hipSuccess) return err;
         if ((err = launch_fill_nan(slot_v(slot, i), copy_bytes, xs)) != hipSuccess) return err;
       }
-      if ((err = hipMemcpyAsync(slot_k(slot, i), k_home[n], copy_bytes, hipMemcpyDeviceToDevice, xs)) != hipSuccess)
-        return err;
-      if ((err = hipMemcpyAsync(slot_v(slot, i), v_home[n], copy_bytes, hipMemcpyDeviceToDevice, xs)) != hipSuccess)
-        return err;
+      if ((err = hipMemcpyAsync(slot_k(slot, i), k_home[n], copy_bytes, copy_kind, xs)) != hipSuccess) return err;
+      if ((err = hipMemcpyAsync(slot_v(slot, i), v_home[n], copy_bytes, copy_kind, xs)) != hipSuccess) return err;
     }
     return err;
   };
