@@ -1,6 +1,6 @@
 // C ABI of libringattn: argument validation (pure host code, before any HIP
 // call), workspace layout, kernel dispatch and the N-step ring driver.
-#include "../../include/ringattn.h"
+#include "ringattn.h"
 
 #include <cmath>
 #include <cstdarg>

@@ -396,10 +396,11 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
           const float p = fast_exp2(__builtin_fmaf(s[kk >> 1][v], sl2, -lse2));
           dsb[kk][e] = (__bf16)(p * (dp[kk >> 1][v] - delta));
         }
+      // consecutive MFMAs update different accumulators (a dependent MFMA waits for the previous one)
 #pragma unroll
-      for (int db = 0; db < D / 32; ++db)
+      for (int kk = 0; kk < 4; ++kk)
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk) dq[db] = mfma(tr_operand<D>(Ks[buf], kk * 16, db * 32, lane), dsb[kk], dq[db]);
+        for (int db = 0; db < D / 32; ++db) dq[db] = mfma(tr_operand<D>(Ks[buf], kk * 16, db * 32, lane), dsb[kk], dq[db]);
       if (more) finish_tile(buf ^ 1);
       __syncthreads();
     }

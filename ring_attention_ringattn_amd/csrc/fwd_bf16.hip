@@ -81,7 +81,7 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs a) {
   __shared__ __attribute__((aligned(1024))) __bf16 Vs[2][BN * D];
   __shared__ __attribute__((aligned(16))) int kvp[2][BN];
   __shared__ __attribute__((aligned(16))) int kvd[2][BN];
-  __shared__ int list[LIST];
+  __shared__ int list[LIST + 1];   // + sentinel
   __shared__ int wave_cnt[NWAVES];
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, g = lane >> 5, j = lane & 31;
@@ -183,21 +183,23 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs a) {
       total += c;
     }
     if (cls != TILE_EMPTY) list[off + my] = t | (cls << 24);
+    if (tid == 0) list[total] = 0;   // read (and ignored) by the look-ahead past the last entry
     __syncthreads();
     if (total == 0) continue;
 
-    issue_tile(__builtin_amdgcn_readfirstlane(list[0]) & 0xffffff, 0);
+    // list entries are workgroup-uniform: keep them scalar so the branches on them stay branches
+    int ent = __builtin_amdgcn_readfirstlane(list[0]);
+    issue_tile(ent & 0xffffff, 0);
     finish_tile(0);
     __syncthreads();
 
     for (int li = 0; li < total; ++li) {
       const int buf = li & 1;
-      // the list entry is workgroup-uniform: keep it scalar so the branches on it stay branches
-      const int ent = __builtin_amdgcn_readfirstlane(list[li]);
       const bool partial = (ent >> 24) == TILE_PARTIAL;
       const int kvalid = a.sk - (ent & 0xffffff) * BN;   // keys of this tile that exist (>= BN: all)
       const bool more = li + 1 < total;
-      if (more) issue_tile(__builtin_amdgcn_readfirstlane(list[li + 1]) & 0xffffff, buf ^ 1);
+      const int ent_next = __builtin_amdgcn_readfirstlane(list[li + 1]);
+      if (more) issue_tile(ent_next & 0xffffff, buf ^ 1);
 
       // ---- S^T = K Q^T (raw scores) ----
       f32x16 s[2];
@@ -267,10 +269,11 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs a) {
 
       // ---- O^T += V^T P^T, V^T from the row-major tile by transpose reads ----
 #pragma unroll
-      for (int db = 0; db < D / 32; ++db)
+      for (int kk = 0; kk < 4; ++kk)
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk) acc[db] = mfma(tr_operand<D>(Vs[buf], kk * 16, db * 32, lane), pf[kk], acc[db]);
+        for (int db = 0; db < D / 32; ++db) acc[db] = mfma(tr_operand<D>(Vs[buf], kk * 16, db * 32, lane), pf[kk], acc[db]);
       if (more) finish_tile(buf ^ 1);
+      ent = ent_next;
       __syncthreads();
     }
   }
