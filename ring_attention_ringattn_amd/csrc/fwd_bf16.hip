@@ -1,8 +1,9 @@
 // Forward ring step, bf16 inputs, fp32 accumulation, on gfx950 MFMA.
 //
-// One workgroup = 4 waves = BM = 128 query rows of one (batch, query head);
-// it walks the key/value block in tiles of BN = 64 keys, skipping tiles that
-// the mask hides entirely (per-tile position/document ranges).  Per tile:
+// One workgroup = 8 waves = BM = 256 query rows of one (batch, query head)
+// (32 rows per wave); it walks the key/value block in tiles of BN = 64 keys,
+// skipping tiles that the mask hides entirely (per-tile position/document
+// ranges).  Per tile and wave:
 //
 //   S^T = K Q^T           v_mfma_f32_32x32x16_bf16, K tile from LDS (A),
 //                         the wave's Q rows held in registers (B)
@@ -20,14 +21,23 @@
 // keys, which is exactly the operand layout; the keys of the V^T operand are
 // then read in natural order.
 //
-// Data movement: K and V tiles go from HBM straight into LDS with buffer
-// loads (no register staging; the buffer range zero-fills keys past the end
-// of the block), double-buffered so the next tile streams in during the
-// current one's MFMAs; one barrier per tile.  Tiles are row-major and
+// Ping-pong schedule.  The softmax of a tile costs about as many issue
+// cycles as its two products, so the workgroup is split into two groups of
+// four waves, one wave of each group per SIMD, running half a period apart
+// and separated by workgroup barriers:
+//
+//   period i, phase X:  leading group   PV(i-1), S(i)      (matrix cores)
+//                       trailing group  softmax(i-1)       (vector ALU)
+//   period i, phase Y:  leading group   softmax(i)
+//                       trailing group  PV(i-1), S(i)
+//
+// so on every SIMD one wave feeds the matrix core while the other computes
+// exponentials.  Both phases of period i read the same two tiles, K(i) and
+// V(i-1); K(i+1) and V(i) stream from HBM straight into LDS (buffer loads,
+// no register staging, zero-fill past the end of the block) during period i
+// into the other halves of double buffers.  Tiles are row-major and
 // swizzled (mfma_tile.h) so the K operand reads and the V transpose reads
 // are free of bank conflicts.
-// Two workgroups fit on a CU, so one workgroup's softmax overlaps the other's
-// MFMAs.
 //
 // Online softmax with a lazily updated maximum: the running maximum m only
 // moves when a tile's maximum exceeds it by more than RESCALE_SLACK (log2
@@ -44,16 +54,21 @@ namespace ra {
 
 namespace {
 
-constexpr int BN = 64;      // keys per tile (== TILE)
-constexpr int NWAVES = 4;
-constexpr int BM = NWAVES * 32;   // query rows per workgroup (32 per wave)
-constexpr int LIST = 256;   // tile-list chunk (one tile per thread when building it)
+constexpr int BN = 64;             // keys per tile (== TILE)
+constexpr int NWAVES = 8;          // two groups of four (one wave of each per SIMD)
+constexpr int BM = NWAVES * 32;    // query rows per workgroup (32 per wave)
+constexpr int LIST = NWAVES * 64;  // tile-list chunk (one tile per thread when building it)
+constexpr int NBUF = 4;            // K/V tile buffers: the tiles of periods i .. i+3
 constexpr float RESCALE_SLACK = 8.0f;
+#ifndef RA_FWD_AHEAD
+#define RA_FWD_AHEAD 3      // operand reads issued ahead of the MFMA that uses them
+#endif
 
 template <int D>
 struct Cfg {
-  static constexpr int CHUNKS = BN * D * 2 / 1024;   // 1 KB buffer->LDS chunks per tile
+  static constexpr int CHUNKS = BN * D * 2 / 1024;   // 1 KB buffer->LDS chunks per tile and operand
   static constexpr int CPW = CHUNKS / NWAVES;        // ... per wave
+  static_assert(CPW * NWAVES == CHUNKS, "tile chunks must divide over the waves");
 };
 
 // Workgroup -> (batch, query head, query tile).  Hardware hands consecutive
@@ -75,16 +90,18 @@ __device__ __forceinline__ void map_block(int n_qt, int hq, int hkv, int total, 
 }  // namespace
 
 template <int D>
-__global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs a) {
+__global__ __launch_bounds__(NWAVES * 64, 1) void fwd_bf16_kernel(FwdArgs a) {
   using C = Cfg<D>;
-  __shared__ __attribute__((aligned(1024))) __bf16 Ks[2][BN * D];
-  __shared__ __attribute__((aligned(1024))) __bf16 Vs[2][BN * D];
-  __shared__ __attribute__((aligned(16))) int kvp[2][BN];
-  __shared__ __attribute__((aligned(16))) int kvd[2][BN];
-  __shared__ int list[LIST + 1];   // + sentinel
+  __shared__ __attribute__((aligned(1024))) __bf16 Ks[NBUF][BN * D];
+  __shared__ __attribute__((aligned(1024))) __bf16 Vs[NBUF][BN * D];
+  __shared__ __attribute__((aligned(16))) int kvp[NBUF][BN];   // positions of the keys of K buffer i
+  __shared__ __attribute__((aligned(16))) int kvd[NBUF][BN];   // ... and their documents
+  __shared__ int list[LIST];
   __shared__ int wave_cnt[NWAVES];
 
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, g = lane >> 5, j = lane & 31;
+  const int tid = threadIdx.x, lane = tid & 63, g = lane >> 5, j = lane & 31;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const bool leading = wave < NWAVES / 2;
   const int n_qt = (a.sq + BM - 1) / BM;
   int b, h, qt;
   map_block(n_qt, a.hq, a.hkv, n_qt * a.hq * a.B, b, h, qt);
@@ -127,42 +144,142 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs a) {
   const int nkt = n_tiles(a.sk);
   const bool no_skip = (a.flags & FLAG_NO_SKIP) != 0;
   const float sl2 = a.scale_log2;
+  const bool no_causal = mask == MASK_NONE, no_doc = mask != MASK_DOC_CAUSAL;
 
   // Per-lane byte offsets (within a tile) of this lane's 16-byte unit of each
-  // of the wave's CPW buffer->LDS chunks: chunk q = c*4 + wave covers LDS
-  // units [64q, 64q+64); unit p holds row p/U, logical column (p%U) ^ swz(row).
+  // of the wave's CPW buffer->LDS chunks: chunk q = c*NWAVES + wave covers
+  // LDS units [64q, 64q+64); unit p holds row p/U, logical column
+  // (p%U) ^ swz(row).
   int voff[C::CPW];
 #pragma unroll
   for (int c = 0; c < C::CPW; ++c) voff[c] = chunk_voff<D>(c * NWAVES + wave, lane, rsb);
-  int preg = POS_INVALID, dreg = 0;
 
-  // Start streaming tile `tile` into LDS buffer `buf`.
-  auto issue_tile = [&] __device__(int tile, int buf) {
+  // Start streaming the K rows (with the key positions and documents, wave 0)
+  // / the V rows of the tile at list entry li into buffer li % NBUF.  Every
+  // wave issues its share; keys past the end of the block read as zero.
+  auto issue_k = [&] __device__(int li, int tile) {
+    const int buf = li % NBUF;
     const int kbase = tile * BN;
     const int rows = min(BN, a.sk - kbase);
+    if (wave == 0) {
+      dma4(a.kv_pos + kbase, rows * 4, (RA_LDS void*)&kvp[buf][0], lane * 4);
+      if (mask == MASK_DOC_CAUSAL) dma4(a.kv_doc + kbase, rows * 4, (RA_LDS void*)&kvd[buf][0], lane * 4);
+    }
     const __bf16* kb = kptr + (size_t)kbase * a.kvs.s;
+#pragma unroll
+    for (int c = 0; c < C::CPW; ++c)
+      dma16(kb, rows * rsb, (RA_LDS void*)&Ks[buf][(c * NWAVES + wave) * 512], voff[c]);
+  };
+  auto issue_v = [&] __device__(int li, int tile) {
+    const int buf = li % NBUF;
+    const int kbase = tile * BN;
+    const int rows = min(BN, a.sk - kbase);
     const __bf16* vb = vptr + (size_t)kbase * a.kvs.s;
 #pragma unroll
-    for (int c = 0; c < C::CPW; ++c) {
-      const int q = c * NWAVES + wave;
-      dma16(kb, rows * rsb, (RA_LDS void*)&Ks[buf][q * 512], voff[c]);
-      dma16(vb, rows * rsb, (RA_LDS void*)&Vs[buf][q * 512], voff[c]);
-    }
-    if (tid < BN) {
-      const int key = kbase + tid;
-      const bool ok = key < a.sk;
-      preg = ok ? a.kv_pos[key] : POS_INVALID;
-      dreg = (ok && mask == MASK_DOC_CAUSAL) ? a.kv_doc[key] : 0;
-    }
-  };
-  auto finish_tile = [&] __device__(int buf) {
-    if (tid < BN) {
-      kvp[buf][tid] = preg;
-      kvd[buf][tid] = dreg;
-    }
-    wait_vmem();   // this thread's buffer->LDS loads have landed
+    for (int c = 0; c < C::CPW; ++c)
+      dma16(vb, rows * rsb, (RA_LDS void*)&Vs[buf][(c * NWAVES + wave) * 512], voff[c]);
   };
 
+  // S^T = K Q^T (raw scores) of the tile in K buffer `buf`.
+  auto scores = [&] __device__(int buf, f32x16(&s)[2]) {
+    s[0] = f32x16{};
+    s[1] = f32x16{};
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) {
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb) {
+        const bf16x8 kf = *(const bf16x8*)(&Ks[buf][tile_off<D>(mb * 32 + swap23(j), ks * 16 + g * 8)]);
+        s[mb] = mfma(kf, qf[ks], s[mb]);
+      }
+    }
+    // issue order: operand reads run AHEAD products ahead of their MFMA (one wave per
+    // SIMD feeds the matrix core in this phase, so nothing else hides the LDS latency)
+    constexpr int N = D / 8, AHEAD = RA_FWD_AHEAD;
+    __builtin_amdgcn_sched_group_barrier(0x100, AHEAD, 0);
+#pragma unroll
+    for (int n = 0; n < N; ++n) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      if (n + AHEAD < N) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+  };
+
+  // Mask (partial tiles only) and online softmax of list entry `li` (key
+  // positions in buffer `buf`): rescales acc/l_run when the maximum moves,
+  // returns the probabilities as bf16 P^T operands.
+  // lane (g, j), value v of block mb holds key mb*32 + 16*(v/8) + 8*g + v%8 for query j.
+  auto softmax = [&] __device__(int li, int buf, f32x16(&s)[2], bf16x8(&pf)[4]) {
+    // list entries are workgroup-uniform: keep them scalar so the branches on them stay branches
+    const int ent = __builtin_amdgcn_readfirstlane(list[li]);
+    const bool partial = (ent >> 24) == TILE_PARTIAL;
+    const int kvalid = a.sk - (ent & 0xffffff) * BN;   // keys of this tile that exist (>= BN: all)
+    if (partial) {
+      asm volatile("" ::: "memory");   // keep this a real branch: full tiles must not pay for masking
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          const int base = mb * 32 + 16 * hh + 8 * g;
+          const i32x4 p0 = *(const i32x4*)&kvp[buf][base], p1 = *(const i32x4*)&kvp[buf][base + 4];
+          const i32x4 d0 = *(const i32x4*)&kvd[buf][base], d1 = *(const i32x4*)&kvd[buf][base + 4];
+          const int lim = kvalid - base;   // e < lim: key base + e exists
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const int kp = e < 4 ? p0[e] : p1[e - 4];
+            const int kd = e < 4 ? d0[e] : d1[e - 4];
+            // bitwise, not short-circuit: one select per score, no branches
+            const bool ok = (e < lim) & (no_causal | (kp <= qpos)) & (no_doc | (kd == qdoc));
+            s[mb][hh * 8 + e] = ok ? s[mb][hh * 8 + e] : -INFINITY;
+          }
+        }
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s[mb][v]);
+    const float mt = pair_max(mx) * sl2;   // tile maximum, scaled log2 units (-inf stays -inf)
+    // move the running maximum only when this tile would overflow the slack
+    const bool grow = mt > m_run + RESCALE_SLACK;
+    if (__any(grow)) {
+      // lanes that do not grow keep their maximum (alpha = 1; their m may still be -inf)
+      const float alpha = grow ? fast_exp2(m_run - mt) : 1.f;   // 0 when growing from -inf
+      m_run = grow ? mt : m_run;
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) acc[db] *= alpha;
+    }
+    const float neg_m = m_run == -INFINITY ? 0.f : -m_run;
+    // probabilities: fp32 for the row sum (the LSE needs it; a sum of the bf16-rounded
+    // values would be off by up to 2^-9 relative), bf16 for the PV product
+    float rs = 0.f;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float p = fast_exp2(__builtin_fmaf(s[kk >> 1][(kk & 1) * 8 + e], sl2, neg_m));
+        rs += p;
+        pf[kk][e] = (__bf16)p;
+      }
+    l_run += rs;
+  };
+
+  // O^T += V^T P^T, V^T from the row-major tile in V buffer `buf` by transpose reads.
+  auto pv = [&] __device__(int buf, const bf16x8(&pf)[4]) {
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) acc[db] = mfma(tr_operand<D>(Vs[buf], kk * 16, db * 32, lane), pf[kk], acc[db]);
+    constexpr int N = D / 8, AHEAD = RA_FWD_AHEAD;   // as in scores(); two transpose reads per operand
+    __builtin_amdgcn_sched_group_barrier(0x100, 2 * AHEAD, 0);
+#pragma unroll
+    for (int n = 0; n < N; ++n) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      if (n + AHEAD < N) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    }
+  };
+
+  f32x16 s[2];
+  bf16x8 pf[4];
   for (int c0 = 0; c0 < nkt; c0 += LIST) {
     // ---- compact the non-empty tiles of this chunk into `list` ----
     const int t = c0 + tid;
@@ -183,99 +300,41 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs a) {
       total += c;
     }
     if (cls != TILE_EMPTY) list[off + my] = t | (cls << 24);
-    if (tid == 0) list[total] = 0;   // read (and ignored) by the look-ahead past the last entry
     __syncthreads();
+    total = __builtin_amdgcn_readfirstlane(total);
     if (total == 0) continue;
+    auto tile_of = [&] __device__(int li) { return __builtin_amdgcn_readfirstlane(list[li]) & 0xffffff; };
 
-    // list entries are workgroup-uniform: keep them scalar so the branches on them stay branches
-    int ent = __builtin_amdgcn_readfirstlane(list[0]);
-    issue_tile(ent & 0xffffff, 0);
-    finish_tile(0);
+    // prologue: K(0..2), V(0..1); V(-1) := 0 and P := 0 so that period 0's PV adds nothing
+    for (int t = 0; t < min(3, total); ++t) issue_k(t, tile_of(t));
+    for (int t = 0; t < min(2, total); ++t) issue_v(t, tile_of(t));
+    for (int e = tid * 8; e < BN * D; e += NWAVES * 64 * 8) *(bf16x8*)&Vs[NBUF - 1][e] = bf16x8{};
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) pf[kk] = bf16x8{};
+    wait_vmem();
     __syncthreads();
 
-    for (int li = 0; li < total; ++li) {
-      const int buf = li & 1;
-      const bool partial = (ent >> 24) == TILE_PARTIAL;
-      const int kvalid = a.sk - (ent & 0xffffff) * BN;   // keys of this tile that exist (>= BN: all)
-      const bool more = li + 1 < total;
-      const int ent_next = __builtin_amdgcn_readfirstlane(list[li + 1]);
-      if (more) issue_tile(ent_next & 0xffffff, buf ^ 1);
-
-      // ---- S^T = K Q^T (raw scores) ----
-      f32x16 s[2];
-      s[0] = f32x16{};
-      s[1] = f32x16{};
-#pragma unroll
-      for (int ks = 0; ks < D / 16; ++ks) {
-#pragma unroll
-        for (int mb = 0; mb < 2; ++mb) {
-          const bf16x8 kf = *(const bf16x8*)(&Ks[buf][tile_off<D>(mb * 32 + swap23(j), ks * 16 + g * 8)]);
-          s[mb] = mfma(kf, qf[ks], s[mb]);
-        }
-      }
-
-      // ---- mask (partial tiles only), online softmax ----
-      // lane (g, j), value v of block mb holds key mb*32 + 16*(v/8) + 8*g + v%8 for query j.
-      if (partial) {
-        asm volatile("" ::: "memory");   // keep this a real branch: full tiles must not pay for masking
-#pragma unroll
-        for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-          for (int hh = 0; hh < 2; ++hh) {
-            const int base = mb * 32 + 16 * hh + 8 * g;
-            const i32x4 p0 = *(const i32x4*)&kvp[buf][base], p1 = *(const i32x4*)&kvp[buf][base + 4];
-            const i32x4 d0 = *(const i32x4*)&kvd[buf][base], d1 = *(const i32x4*)&kvd[buf][base + 4];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-              const int kp = e < 4 ? p0[e] : p1[e - 4];
-              const int kd = e < 4 ? d0[e] : d1[e - 4];
-              bool ok = base + e < kvalid;
-              if (mask != MASK_NONE) ok = ok && kp <= qpos;
-              if (mask == MASK_DOC_CAUSAL) ok = ok && kd == qdoc;
-              s[mb][hh * 8 + e] = ok ? s[mb][hh * 8 + e] : -INFINITY;
-            }
-          }
-      }
-      float mx = -INFINITY;
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s[mb][v]);
-      const float mt = pair_max(mx) * sl2;   // tile maximum, scaled log2 units (-inf stays -inf)
-      // move the running maximum only when this tile would overflow the slack
-      const bool grow = mt > m_run + RESCALE_SLACK;
-      if (__any(grow)) {
-        // lanes that do not grow keep their maximum (alpha = 1; their m may still be -inf)
-        const float alpha = grow ? fast_exp2(m_run - mt) : 1.f;   // 0 when growing from -inf
-        m_run = grow ? mt : m_run;
-        l_run *= alpha;
-#pragma unroll
-        for (int db = 0; db < D / 32; ++db) acc[db] *= alpha;
-      }
-      const float neg_m = m_run == -INFINITY ? 0.f : -m_run;
-      // probabilities: fp32 for the row sum (the LSE needs it; a sum of the bf16-rounded
-      // values would be off by up to 2^-9 relative), bf16 for the PV product
-      bf16x8 pf[4];
-      float rs = 0.f;
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float p = fast_exp2(__builtin_fmaf(s[kk >> 1][(kk & 1) * 8 + e], sl2, neg_m));
-          rs += p;
-          pf[kk][e] = (__bf16)p;
-        }
-      l_run += rs;
-
-      // ---- O^T += V^T P^T, V^T from the row-major tile by transpose reads ----
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk)
-#pragma unroll
-        for (int db = 0; db < D / 32; ++db) acc[db] = mfma(tr_operand<D>(Vs[buf], kk * 16, db * 32, lane), pf[kk], acc[db]);
-      if (more) finish_tile(buf ^ 1);
-      ent = ent_next;
+    // Both groups run the same sequence, the trailing one shifted by one
+    // barrier, so that while one group is in its matrix phase the other is in
+    // its softmax phase.  Period i reads K(i) and V(i-1); in its softmax phase
+    // each group issues its share of K(i+3) and V(i+2).  A wave's loads are
+    // complete before the barrier that precedes the period that needs them:
+    // the leading group waits at the start of its softmax phase, the trailing
+    // group at the end of its matrix phase (vmcnt(0): buffer->LDS loads are
+    // not relied on to retire in issue order).
+    if (!leading) __syncthreads();
+    for (int i = 0; i <= total; ++i) {
+      pv((i + NBUF - 1) % NBUF, pf);
+      scores(i % NBUF, s);
+      if (!leading) wait_vmem();
+      __syncthreads();
+      if (leading) wait_vmem();
+      if (i + 3 < total) issue_k(i + 3, tile_of(i + 3));
+      if (i + 2 < total) issue_v(i + 2, tile_of(i + 2));
+      if (i < total) softmax(i, i % NBUF, s, pf);
       __syncthreads();
     }
+    if (leading) __syncthreads();
   }
 
   // ---- epilogue: normalise, merge into (o_acc, lse), optionally write out ----
@@ -316,8 +375,8 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs a) {
 hipError_t launch_fwd_bf16(const FwdArgs& a, int d, hipStream_t st) {
   const long blocks = (long)((a.sq + BM - 1) / BM) * a.hq * a.B;
   if (blocks == 0) return hipSuccess;
-  if (d == 128) fwd_bf16_kernel<128><<<(unsigned)blocks, 256, 0, st>>>(a);
-  else fwd_bf16_kernel<64><<<(unsigned)blocks, 256, 0, st>>>(a);
+  if (d == 128) fwd_bf16_kernel<128><<<(unsigned)blocks, NWAVES * 64, 0, st>>>(a);
+  else fwd_bf16_kernel<64><<<(unsigned)blocks, NWAVES * 64, 0, st>>>(a);
   return hipGetLastError();
 }
 

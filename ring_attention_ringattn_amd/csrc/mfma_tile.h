@@ -60,6 +60,12 @@ __device__ __forceinline__ void dma16(const void* base, int nbytes, RA_LDS void*
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, dst, 16, voff, 0, 0, 0);
 }
 
+// Copy 4 bytes per lane from base + voff into LDS at dst + 4*lane (zero past nbytes).
+__device__ __forceinline__ void dma4(const void* base, int nbytes, RA_LDS void* dst, int voff) {
+  const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, nbytes, RSRC_WORD3);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, dst, 4, voff, 0, 0, 0);
+}
+
 __device__ __forceinline__ s16x4 lds_read_tr16(const __bf16* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((RA_LDS s16x4*)p);
 }
@@ -75,6 +81,12 @@ __device__ __forceinline__ float pair_sum(float x) {
 }
 
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }   // vmcnt(0)
+// vmcnt(N), N < 16: at most N of this wave's vector memory operations still outstanding
+template <int N>
+__device__ __forceinline__ void wait_vmem_n() {
+  static_assert(N >= 0 && N < 16, "vmcnt immediate");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | N);
+}
 
 __device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);

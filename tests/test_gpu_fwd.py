@@ -13,7 +13,7 @@ import torch
 import oracle
 import ring_attention_ringattn_amd as ra
 import synthetic
-from tests.gpu_util import Ring, dev, max_abs, oracle_rows, print_case, MASKS, TORCH_DT
+from tests.gpu_util import Ring, dev, max_abs, oracle_rows, print_case, thd_view, MASKS, TORCH_DT
 
 pytestmark = pytest.mark.gpu
 
@@ -84,13 +84,21 @@ CASES = [
     ("bf16", 64, 2, 2, 1, 64, 1000, "none"),
     ("f32", 128, 1, 2, 1, 100, 150, "causal"),
     ("f32", 64, 2, 3, 3, 65, 70, "doc_causal"),
+    # long enough key blocks (>= 5 tiles) that tiles stream in while others are being used
+    ("bf16", 128, 1, 4, 2, 300, 1100, "causal"),
+    ("bf16", 128, 1, 4, 2, 300, 1100, "doc_causal"),
+    ("bf16", 64, 1, 4, 2, 300, 1100, "doc_causal"),
+    # token-major [S, H, D] storage (strided views)
+    ("bf16", 128, 1, 4, 2, 300, 1100, "causal", "thd"),
+    ("bf16", 128, 1, 4, 2, 300, 1100, "doc_causal", "thd"),
 ]
 
 
 @pytest.mark.parametrize("case", CASES, ids=lambda c: "-".join(map(str, c)))
 def test_step_fwd_ragged_edges(case):
     """Two manual steps (FIRST, then LAST) over ragged sizes with scattered positions and documents."""
-    dtype, d, B, hq, hkv, sq, sk, mask = case
+    dtype, d, B, hq, hkv, sq, sk, mask = case[:8]
+    layout = case[8] if len(case) > 8 else "bhsd"
     print_case(f"step_fwd {case}")
     rng = np.random.default_rng(zlib.crc32(repr(case).encode()))
     wdt = torch.float32 if dtype == "f32" else torch.bfloat16
@@ -108,8 +116,11 @@ def test_step_fwd_ragged_edges(case):
     lse = torch.zeros(B, hq, sq, device="cuda")
     out = torch.full((B, hq, sq, d), float("nan"), dtype=wdt, device="cuda")
     dm = mask == "doc_causal"
+    put = (lambda a: thd_view(dev(a, wdt))) if layout == "thd" else (lambda a: dev(a, wdt))
+    if layout == "thd":
+        out = thd_view(out)
     for step, (k, v, kp, kd) in enumerate(((k1, v1, kp1, kd1), (k2, v2, kp2, kd2))):
-        ra.ringattn_step_fwd(dev(q, wdt), dev(k, wdt), dev(v, wdt), o_acc, lse, out, dev(qp, torch.int32),
+        ra.ringattn_step_fwd(put(q), put(k), put(v), o_acc, lse, out, dev(qp, torch.int32),
                              dev(kp, torch.int32), dev(qd, torch.int32) if dm else None,
                              dev(kd, torch.int32) if dm else None, mask_mode=MASKS[mask],
                              flags=ra.RA_STEP_FIRST if step == 0 else ra.RA_STEP_LAST)
@@ -124,6 +135,29 @@ def test_step_fwd_ragged_edges(case):
     assert max_abs(got_l[fin], L[fin]) <= tol_l
     assert max_abs(o_acc.cpu().numpy(), O) <= tol_o          # masked rows: O = 0 on both sides
     assert max_abs(out.float().cpu().numpy(), O) <= tol_o
+
+
+@pytest.mark.parametrize("d", [128, 64])
+def test_step_fwd_tile_lists_with_gaps(d):
+    """Document-causal step of the last of 4 contiguous shards against its own block: the
+    non-empty key tiles of a query tile start past tile 0 and skip tiles (documents end)."""
+    print_case(f"step_fwd doc-causal diagonal block, D={d}")
+    rng = np.random.default_rng(5)
+    rnd = lambda *s: synthetic.bf16_round(0.5 * rng.standard_normal(s).astype(np.float32))
+    cu = np.array([0, 313, 1847, 3151, 3314, 3524, 3683, 4096], np.int32)
+    doc = oracle.docs_from_cu_seqlens(cu, 4096)
+    p = np.arange(3072, 4096, dtype=np.int32)
+    q, k, v = rnd(1, 4, 1024, d), rnd(1, 2, 1024, d), rnd(1, 2, 1024, d)
+    o = torch.zeros(1, 4, 1024, d, device="cuda")
+    lse = torch.zeros(1, 4, 1024, device="cuda")
+    bf = torch.bfloat16
+    ra.ringattn_step_fwd(dev(q, bf), dev(k, bf), dev(v, bf), o, lse, None, dev(p, torch.int32), dev(p, torch.int32),
+                         dev(doc[p], torch.int32), dev(doc[p], torch.int32), mask_mode=ra.RA_MASK_DOC_CAUSAL,
+                         flags=ra.RA_STEP_FIRST)
+    torch.cuda.synchronize()
+    O, L = oracle.attention_forward(q, k, v, p, p, "doc_causal", doc[p], doc[p])
+    assert max_abs(lse.cpu().numpy(), L) <= 1e-3
+    assert max_abs(o.cpu().numpy(), O) <= 1e-2
 
 
 def test_empty_and_fully_masked():
