@@ -203,13 +203,11 @@ __global__ __launch_bounds__(NWAVES * 64, 1) void fwd_bf16_kernel(FwdArgs a) {
     }
   };
 
-  // Mask (partial tiles only) and online softmax of list entry `li` (key
-  // positions in buffer `buf`): rescales acc/l_run when the maximum moves,
+  // Mask (partial tiles only) and online softmax of the tile of list entry
+  // `ent` (workgroup-uniform, scalar; key positions in buffer `buf`): rescales acc/l_run when the maximum moves,
   // returns the probabilities as bf16 P^T operands.
   // lane (g, j), value v of block mb holds key mb*32 + 16*(v/8) + 8*g + v%8 for query j.
-  auto softmax = [&] __device__(int li, int buf, f32x16(&s)[2], bf16x8(&pf)[4]) {
-    // list entries are workgroup-uniform: keep them scalar so the branches on them stay branches
-    const int ent = __builtin_amdgcn_readfirstlane(list[li]);
+  auto softmax = [&] __device__(int ent, int buf, f32x16(&s)[2], bf16x8(&pf)[4]) {
     const bool partial = (ent >> 24) == TILE_PARTIAL;
     const int kvalid = a.sk - (ent & 0xffffff) * BN;   // keys of this tile that exist (>= BN: all)
     if (partial) {
@@ -317,21 +315,21 @@ __global__ __launch_bounds__(NWAVES * 64, 1) void fwd_bf16_kernel(FwdArgs a) {
     // Both groups run the same sequence, the trailing one shifted by one
     // barrier, so that while one group is in its matrix phase the other is in
     // its softmax phase.  Period i reads K(i) and V(i-1); in its softmax phase
-    // each group issues its share of K(i+3) and V(i+2).  A wave's loads are
-    // complete before the barrier that precedes the period that needs them:
-    // the leading group waits at the start of its softmax phase, the trailing
-    // group at the end of its matrix phase (vmcnt(0): buffer->LDS loads are
-    // not relied on to retire in issue order).
+    // each group first waits for its own earlier loads (issued a period, i.e.
+    // two barriers, before) and then issues its share of K(i+3) and V(i+2),
+    // which period i+3 reads: the next wait, and two barriers, come first.
     if (!leading) __syncthreads();
     for (int i = 0; i <= total; ++i) {
       pv((i + NBUF - 1) % NBUF, pf);
       scores(i % NBUF, s);
-      if (!leading) wait_vmem();
       __syncthreads();
-      if (leading) wait_vmem();
-      if (i + 3 < total) issue_k(i + 3, tile_of(i + 3));
-      if (i + 2 < total) issue_v(i + 2, tile_of(i + 2));
-      if (i < total) softmax(i, i % NBUF, s, pf);
+      wait_vmem();
+      // list entries used in this phase: one LDS round trip for all three
+      const int e0 = list[min(i, LIST - 1)], e2 = list[min(i + 2, LIST - 1)], e3 = list[min(i + 3, LIST - 1)];
+      // list entries are workgroup-uniform: keep them scalar so the branches on them stay branches
+      if (i + 3 < total) issue_k(i + 3, __builtin_amdgcn_readfirstlane(e3) & 0xffffff);
+      if (i + 2 < total) issue_v(i + 2, __builtin_amdgcn_readfirstlane(e2) & 0xffffff);
+      if (i < total) softmax(__builtin_amdgcn_readfirstlane(e0), i % NBUF, s, pf);
       __syncthreads();
     }
     if (leading) __syncthreads();
