@@ -181,7 +181,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
       const bool more = li + 1 < total;
       if (more) issue_tile(__builtin_amdgcn_readfirstlane(list[li + 1]) & 0xffffff, buf ^ 1);
 
-#pragma unroll 1
+#pragma unroll
       for (int mb = 0; mb < 2; ++mb) {
         f32x16 s = {}, dp = {};
 #pragma unroll
