@@ -123,8 +123,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
   int voff[CPW];
 #pragma unroll
   for (int c = 0; c < CPW; ++c) voff[c] = chunk_voff<D>(c * NWAVES + wave, lane, rsb);
-  float sreg = 0.f;
-  int ireg = 0;
+  unsigned rraw = 0;
+  bool rok = false;
 
   // stage query tile `item` (= query head in group * n_qt + tile) into buffer `buf`
   auto issue_tile = [&] __device__(int item, int buf) {
@@ -139,27 +139,30 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
       dma16((const __bf16*)a.q + base, rows * rsb, (RA_LDS void*)&Qs[buf][q * 512], voff[c]);
       dma16((const __bf16*)a.d_o + base, rows * rsb, (RA_LDS void*)&Os[buf][q * 512], voff[c]);
     }
+    // per-row values (wave w: LSE, delta, position, document): one unconditional raw
+    // 4-byte load per thread (rows past the end reread the last row).  Nothing here may
+    // depend on the loaded value, else the wait for it would also wait for the tile loads
+    // above; finish_tile converts it.
     const int row = tid & 63, part = tid >> 6;
-    const bool ok = row < rows;
-    const size_t lrow = ((size_t)b * a.hq + h) * a.sq + q0 + row;
-    if (part == 0) {
-      const float l = ok ? a.lse[lrow] : -INFINITY;
-      sreg = l == -INFINITY ? INFINITY : l * LOG2E;
-    } else if (part == 1) {
-      sreg = ok ? a.delta[lrow] : 0.f;
-    } else if (part == 2) {
-      ireg = ok ? a.q_pos[q0 + row] : -1;
-    } else {
-      ireg = (ok && mask == MASK_DOC_CAUSAL) ? a.q_doc[q0 + row] : 0;
-    }
+    rok = row < rows;
+    const int r = q0 + min(row, rows - 1);
+    const size_t lrow = ((size_t)b * a.hq + h) * a.sq + r;
+    const int* doc = mask == MASK_DOC_CAUSAL ? a.q_doc : a.q_pos;
+    const unsigned* src = part == 0 ? (const unsigned*)(a.lse + lrow)
+                        : part == 1 ? (const unsigned*)(a.delta + lrow)
+                        : part == 2 ? (const unsigned*)(a.q_pos + r) : (const unsigned*)(doc + r);
+    rraw = *src;
   };
   auto finish_tile = [&] __device__(int buf) {
-    const int row = tid & 63, part = tid >> 6;
-    if (part == 0) lse2s[buf][row] = sreg;
-    else if (part == 1) dels[buf][row] = sreg;
-    else if (part == 2) qps[buf][row] = ireg;
-    else qds[buf][row] = ireg;
     wait_vmem();
+    const int row = tid & 63, part = tid >> 6;
+    const float f = __uint_as_float(rraw);
+    const int iv = (int)rraw;
+    // LSE in log2 units; +inf for rows past the end or that see no key (P = 0 there)
+    if (part == 0) lse2s[buf][row] = (rok && f != -INFINITY) ? f * LOG2E : INFINITY;
+    else if (part == 1) dels[buf][row] = rok ? f : 0.f;
+    else if (part == 2) qps[buf][row] = rok ? iv : -1;
+    else qds[buf][row] = (rok && mask == MASK_DOC_CAUSAL) ? iv : 0;
   };
 
   const int n_items = grp * n_qt;
@@ -321,19 +324,19 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
       dma16(kptr + (size_t)kbase * a.kvs.s, rows * rsb, (RA_LDS void*)&Ks[buf][q * 512], voff[c]);
       dma16(vptr + (size_t)kbase * a.kvs.s, rows * rsb, (RA_LDS void*)&Vs[buf][q * 512], voff[c]);
     }
-    if (tid < BKT) {
-      const int key = kbase + tid;
-      const bool ok = key < a.sk;
-      preg = ok ? a.kv_pos[key] : POS_INVALID;
-      dreg = (ok && mask == MASK_DOC_CAUSAL) ? a.kv_doc[key] : 0;
-    }
+    // positions and documents of the tile's keys: unconditional raw loads (keys past the
+    // end reread the last key; the mask drops them by index).  Nothing here may depend on
+    // the loaded values, else the wait for them would also wait for the tile loads above.
+    const int key = kbase + min(tid & (BKT - 1), rows - 1);
+    preg = a.kv_pos[key];
+    dreg = (mask == MASK_DOC_CAUSAL ? a.kv_doc : a.kv_pos)[key];
   };
   auto finish_tile = [&] __device__(int buf) {
+    wait_vmem();
     if (tid < BKT) {
       kvp[buf][tid] = preg;
-      kvd[buf][tid] = dreg;
+      kvd[buf][tid] = mask == MASK_DOC_CAUSAL ? dreg : 0;
     }
-    wait_vmem();
   };
 
   const int nkt = n_tiles(a.sk);

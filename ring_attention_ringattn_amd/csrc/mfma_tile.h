@@ -53,17 +53,42 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 // gfx950-only builtins live in device functions: used directly in a kernel
 // template body they make clang drop the kernel's host-side launch stub.
 
-// Copy 16 bytes per lane from base + voff into LDS at dst + 16*lane; bytes at
-// or past base + nbytes read as zero (buffer range check).
-__device__ __forceinline__ void dma16(const void* base, int nbytes, RA_LDS void* dst, int voff) {
-  const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, nbytes, RSRC_WORD3);
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, dst, 16, voff, 0, 0, 0);
+// Buffer -> LDS loads.  Lane l copies 16 (dma16) or 4 (dma4) bytes from
+// base + voff into LDS at dst + 16*l (4*l); bytes at or past base + nbytes read
+// as zero (buffer range check).  base, nbytes and dst must be wave-uniform.
+//
+// They are issued from inline assembly on purpose: the compiler cannot tell
+// which LDS buffer such a load writes, so for the builtin it makes the next
+// LDS read of any buffer wait for all of them (s_waitcnt vmcnt) -- which
+// serialises the prefetch of the next tile with the reads of the current one.
+// Here the compiler knows nothing of the LDS write, so every reader of a
+// loaded tile must be ordered after the loads explicitly: wait_vmem() by the
+// issuing wave, then a workgroup barrier.  ("memory" keeps the compiler from
+// moving other memory accesses across them; loads it does not count only make
+// its own vmcnt waits stricter, never weaker.)
+__device__ __forceinline__ i32x4 buffer_rsrc(const void* base, int nbytes) {
+  const unsigned long long p = (unsigned long long)base;
+  i32x4 r;
+  r[0] = __builtin_amdgcn_readfirstlane((int)(unsigned)p);
+  r[1] = __builtin_amdgcn_readfirstlane((int)((p >> 32) & 0xffff));   // stride 0
+  r[2] = __builtin_amdgcn_readfirstlane(nbytes);
+  r[3] = RSRC_WORD3;
+  return r;
 }
 
-// Copy 4 bytes per lane from base + voff into LDS at dst + 4*lane (zero past nbytes).
+__device__ __forceinline__ int lds_addr(RA_LDS void* p) {
+  return __builtin_amdgcn_readfirstlane((int)(unsigned)(unsigned long)p);
+}
+
+// The LDS destination goes in M0 (an input operand, so the compiler sets it).
+__device__ __forceinline__ void dma16(const void* base, int nbytes, RA_LDS void* dst, int voff) {
+  asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+               :: "v"(voff), "s"(buffer_rsrc(base, nbytes)), "{m0}"(lds_addr(dst)) : "memory");
+}
+
 __device__ __forceinline__ void dma4(const void* base, int nbytes, RA_LDS void* dst, int voff) {
-  const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, nbytes, RSRC_WORD3);
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, dst, 4, voff, 0, 0, 0);
+  asm volatile("s_nop 0\n\tbuffer_load_dword %0, %1, 0 offen lds"
+               :: "v"(voff), "s"(buffer_rsrc(base, nbytes)), "{m0}"(lds_addr(dst)) : "memory");
 }
 
 __device__ __forceinline__ s16x4 lds_read_tr16(const __bf16* p) {
