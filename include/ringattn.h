@@ -11,6 +11,7 @@
  * followed by combine().  This library implements, on one GPU:
  *
  *   ringattn_step_fwd        attn(Q_i, K_j, V_j) with the combine fused in
+ *   ringattn_fused_fwd       all blocks resident: attention over every block in one launch
  *   ringattn_merge           combine() of two normalised partial results
  *   ringattn_bwd_preprocess  D = rowsum(dO * O), needed by the backward
  *   ringattn_step_bwd        gradient contributions of one block
@@ -65,7 +66,7 @@
 extern "C" {
 #endif
 
-#define RINGATTN_VERSION 1
+#define RINGATTN_VERSION 2
 
 typedef enum {
   RA_OK = 0,
@@ -90,8 +91,13 @@ enum {
   RA_RUN_SERIAL_COPY = 16,   /* copy each block on the compute stream (no overlap) */
   RA_RUN_POISON = 32,        /* fill a staging slot with NaN right before each copy into it */
   RA_RUN_MERGE_KERNEL = 64,  /* forward: step kernel writes a separate partial, then ringattn_merge */
-  RA_RUN_COPY_ENGINE = 128   /* stage blocks with the DMA-engine copy (hipMemcpyDeviceToDeviceNoCU)
+  RA_RUN_COPY_ENGINE = 128,  /* stage blocks with the DMA-engine copy (hipMemcpyDeviceToDeviceNoCU)
                                 instead of a copy kernel that shares the compute units */
+  RA_RUN_ALLGATHER = 256     /* forward pass, all blocks resident (the all-gather rotation): each
+                                emulated rank does ONE ringattn_fused_fwd launch over all n_ranks
+                                home blocks (in ring order) instead of n_ranks steps; no staging
+                                copies, o_acc is not written, out[i] is required.  bf16 only,
+                                n_ranks <= RA_FUSED_MAX_BLOCKS, the whole ring (start 0, stop n). */
 };
 
 enum { RA_PASS_FWD = 1, RA_PASS_BWD = 2 };
@@ -135,6 +141,39 @@ int ringattn_step_fwd(const ra_problem* p, const void* q, const void* k_blk, con
                       const int32_t* q_doc, const int32_t* kv_doc,
                       int mask_mode, int flags, void* workspace, size_t workspace_bytes,
                       void* stream);
+
+/* Most K/V blocks one ringattn_fused_fwd call takes. */
+#define RA_FUSED_MAX_BLOCKS 16
+
+/* Bytes of device workspace ringattn_fused_fwd needs (per-tile ranges of the
+ * queries and of each of the n_blocks blocks). */
+size_t ringattn_fused_workspace_size(const ra_problem* p, int n_blocks);
+
+/*
+ * All-gather forward (the guide's all-gather rotation, "ring attention" page,
+ * section on all-gather versus all-to-all rotation): once every K,V block is
+ * resident, attention of q against all n_blocks blocks in ONE launch.  The
+ * tile list of a query tile spans every block and the online-softmax state
+ * stays in registers across blocks, so unlike a ring of ringattn_step_fwd
+ * calls there is no running fp32 output between blocks; the result is exactly
+ * full attention over the union of the blocks (up to rounding order).
+ *   p->sk                       keys per block; every block has the same size and kv_stride
+ *   k_blocks, v_blocks          host arrays of n_blocks device pointers, [B,Hkv,Sk,D] bf16 (in)
+ *   kv_pos, kv_doc              host arrays of n_blocks device int32 pointers (in; docs only
+ *                               for DOC_CAUSAL, else kv_doc may be NULL)
+ *   lse [B,Hq,Sq] fp32 dense, out [B,Hq,Sq,D] bf16 with q_stride   (device, out)
+ *   workspace                   device, >= ringattn_fused_workspace_size(p, n_blocks) bytes
+ * 1 <= n_blocks <= RA_FUSED_MAX_BLOCKS.  bf16 only (fp32 problems return
+ * RA_ERR_UNSUPPORTED).  flags: 0 or RA_NO_SKIP.  The pointer arrays are read
+ * during the call only.
+ */
+int ringattn_fused_fwd(const ra_problem* p, int n_blocks, const void* q,
+                       const void* const* k_blocks, const void* const* v_blocks,
+                       float* lse, void* out,
+                       const int32_t* q_pos, const int32_t* const* kv_pos,
+                       const int32_t* q_doc, const int32_t* const* kv_doc,
+                       int mask_mode, int flags, void* workspace, size_t workspace_bytes,
+                       void* stream);
 
 /*
  * combine() of two normalised partials over disjoint key sets, in place into b:

@@ -21,15 +21,18 @@ import torch
 
 from . import _lib
 from ._lib import (RA_BF16, RA_F32, RA_MASK_CAUSAL, RA_MASK_DOC_CAUSAL, RA_MASK_NONE, RA_MAX_SK, RA_NO_SKIP,
-                   RA_PASS_BWD, RA_PASS_FWD, RA_RUN_COPY_ENGINE, RA_RUN_MERGE_KERNEL, RA_RUN_POISON,
-                   RA_RUN_SERIAL_COPY, RA_STEP_FIRST, RA_STEP_LAST, RingAttnError)
+                   RA_PASS_BWD, RA_PASS_FWD, RA_RUN_ALLGATHER, RA_RUN_COPY_ENGINE, RA_RUN_MERGE_KERNEL,
+                   RA_RUN_POISON, RA_RUN_SERIAL_COPY, RA_STEP_FIRST, RA_STEP_LAST, RA_FUSED_MAX_BLOCKS,
+                   RingAttnError)
 from . import sharding
 
-__all__ = ["ringattn_step_workspace_size", "ringattn_step_fwd", "ringattn_merge", "ringattn_bwd_preprocess",
+__all__ = ["ringattn_step_workspace_size", "ringattn_step_fwd", "ringattn_fused_workspace_size",
+           "ringattn_fused_fwd", "ringattn_merge", "ringattn_bwd_preprocess",
            "ringattn_step_bwd", "ringattn_run_workspace_size", "ringattn_run", "ringattn_docs_from_cu_seqlens",
            "ringattn_last_error", "ringattn_version", "make_problem", "RingAttnError", "sharding",
            "RA_MASK_NONE", "RA_MASK_CAUSAL", "RA_MASK_DOC_CAUSAL", "RA_STEP_FIRST", "RA_STEP_LAST", "RA_NO_SKIP",
-           "RA_RUN_SERIAL_COPY", "RA_RUN_POISON", "RA_RUN_MERGE_KERNEL", "RA_RUN_COPY_ENGINE", "RA_PASS_FWD",
+           "RA_RUN_SERIAL_COPY", "RA_RUN_POISON", "RA_RUN_MERGE_KERNEL", "RA_RUN_COPY_ENGINE", "RA_RUN_ALLGATHER",
+           "RA_FUSED_MAX_BLOCKS", "RA_PASS_FWD",
            "RA_PASS_BWD",
            "RA_F32", "RA_BF16", "RA_MAX_SK"]
 
@@ -109,6 +112,39 @@ def ringattn_step_fwd(q, k_blk, v_blk, o_acc, lse, out, q_pos, kv_pos, q_doc=Non
     return _lib.check(lib.ringattn_step_fwd(
         ctypes.byref(p), _ptr(q), _ptr(k_blk), _ptr(v_blk), _ptr(o_acc), _ptr(lse), _ptr(out), _ptr(q_pos),
         _ptr(kv_pos), _ptr(q_doc), _ptr(kv_doc), mask_mode, flags, _ptr(ws), ws.numel(), _stream(stream)))
+
+
+def ringattn_fused_workspace_size(q: torch.Tensor, k: torch.Tensor, n_blocks: int) -> int:
+    p = make_problem(q, k)
+    return _lib.load().ringattn_fused_workspace_size(ctypes.byref(p), n_blocks)
+
+
+def _c_ptrs(ts):
+    """ctypes array of the tensors' device pointers (kept alive by the caller for the call)."""
+    return (ctypes.c_void_p * len(ts))(*[t.data_ptr() for t in ts])
+
+
+def ringattn_fused_fwd(q, k_blocks, v_blocks, lse, out, q_pos, kv_pos, q_doc=None, kv_doc=None,
+                       mask_mode=RA_MASK_CAUSAL, flags=0, workspace=None, stream=None, softmax_scale=0.0):
+    """Attention of q over every resident block in one launch (all-gather mode); see
+    ringattn_fused_fwd in the header.  k_blocks, v_blocks, kv_pos (and kv_doc) are lists."""
+    lib = _lib.load()
+    n = len(k_blocks)
+    if len(v_blocks) != n or len(kv_pos) != n or (kv_doc is not None and len(kv_doc) != n):
+        raise ValueError("k_blocks, v_blocks, kv_pos (and kv_doc) must have one entry per block")
+    for kb, vb in zip(k_blocks, v_blocks):
+        if kb.stride() != k_blocks[0].stride() or kb.shape != k_blocks[0].shape or vb.stride() != kb.stride() \
+                or vb.shape != kb.shape:
+            raise ValueError("every K and V block must have one shape and one set of strides")
+    if out.stride() != q.stride():
+        raise ValueError("out must have the strides of q")
+    p = make_problem(q, k_blocks[0], softmax_scale)
+    need = lib.ringattn_fused_workspace_size(ctypes.byref(p), n)
+    ws = _workspace(need, q.device, workspace)
+    kd = _c_ptrs(kv_doc) if kv_doc is not None else None
+    return _lib.check(lib.ringattn_fused_fwd(
+        ctypes.byref(p), n, _ptr(q), _c_ptrs(k_blocks), _c_ptrs(v_blocks), _ptr(lse), _ptr(out), _ptr(q_pos),
+        _c_ptrs(kv_pos), _ptr(q_doc), kd, mask_mode, flags, _ptr(ws), ws.numel(), _stream(stream)))
 
 
 def ringattn_merge(o_a, lse_a, o_b, lse_b, stream=None):

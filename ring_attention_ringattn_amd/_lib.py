@@ -16,12 +16,14 @@ RA_OK, RA_ERR_INVALID, RA_ERR_UNSUPPORTED, RA_ERR_WORKSPACE, RA_ERR_HIP = 0, -1,
 RA_MASK_NONE, RA_MASK_CAUSAL, RA_MASK_DOC_CAUSAL = 0, 1, 2
 RA_F32, RA_BF16 = 0, 1
 RA_STEP_FIRST, RA_STEP_LAST, RA_NO_SKIP = 1, 2, 4
-RA_RUN_SERIAL_COPY, RA_RUN_POISON, RA_RUN_MERGE_KERNEL, RA_RUN_COPY_ENGINE = 16, 32, 64, 128
+RA_RUN_SERIAL_COPY, RA_RUN_POISON, RA_RUN_MERGE_KERNEL, RA_RUN_COPY_ENGINE, RA_RUN_ALLGATHER = 16, 32, 64, 128, 256
 RA_PASS_FWD, RA_PASS_BWD = 1, 2
 RA_MAX_SK = 262144
+RA_FUSED_MAX_BLOCKS = 16
 
 # every function include/ringattn.h declares
-EXPORTS = ("ringattn_step_workspace_size", "ringattn_step_fwd", "ringattn_merge", "ringattn_bwd_preprocess",
+EXPORTS = ("ringattn_step_workspace_size", "ringattn_step_fwd", "ringattn_fused_workspace_size", "ringattn_fused_fwd",
+           "ringattn_merge", "ringattn_bwd_preprocess",
            "ringattn_step_bwd", "ringattn_run_workspace_size", "ringattn_run", "ringattn_docs_from_cu_seqlens",
            "ringattn_last_error", "ringattn_version")
 
@@ -47,6 +49,9 @@ _SIG = {
     "ringattn_step_workspace_size": (ctypes.c_size_t, [ctypes.POINTER(RaProblem)]),
     "ringattn_step_fwd": (_I, [ctypes.POINTER(RaProblem), _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _P,
                                ctypes.c_size_t, _P]),
+    "ringattn_fused_workspace_size": (ctypes.c_size_t, [ctypes.POINTER(RaProblem), _I]),
+    "ringattn_fused_fwd": (_I, [ctypes.POINTER(RaProblem), _I, _P, _PP, _PP, _P, _P, _P, _PP, _P, _PP, _I, _I, _P,
+                                ctypes.c_size_t, _P]),
     "ringattn_merge": (_I, [ctypes.POINTER(RaProblem), _P, _P, _P, _P, _P]),
     "ringattn_bwd_preprocess": (_I, [ctypes.POINTER(RaProblem), _P, _P, _P, _P]),
     "ringattn_step_bwd": (_I, [ctypes.POINTER(RaProblem), _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I,

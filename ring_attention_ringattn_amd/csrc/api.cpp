@@ -133,6 +133,10 @@ FwdArgs make_fwd(const ra_problem* p, const void* q, const void* k, const void* 
   a.scale = eff_scale(p);
   a.scale_log2 = a.scale * 1.4426950408889634f;
   a.mask = mask; a.flags = flags;
+  a.n_blocks = 1;
+  for (int j = 0; j < MAX_FUSED_BLOCKS; ++j) {
+    a.kb[j] = k; a.vb[j] = v; a.kposb[j] = kv_pos; a.kdocb[j] = kv_doc; a.ktilesb[j] = kt;
+  }
   return a;
 }
 
@@ -208,6 +212,69 @@ int ringattn_step_fwd(const ra_problem* p, const void* q, const void* k_blk, con
   FwdArgs a = make_fwd(p, q, k_blk, v_blk, o_acc, lse, out, q_pos, kv_pos, q_doc, kv_doc, t.q, t.kv, mask_mode, flags);
   e = enqueue_fwd(p, a, st);
   if (e != hipSuccess) return hip_fail(e, "forward step kernel launch");
+  return ok();
+}
+
+size_t ringattn_fused_workspace_size(const ra_problem* p, int n_blocks) {
+  if (check_problem(p)) return 0;
+  if (n_blocks < 1 || n_blocks > RA_FUSED_MAX_BLOCKS) return 0;
+  return align256((size_t)n_tiles(p->sq) * sizeof(TileRange)) +
+         (size_t)n_blocks * align256((size_t)n_tiles(p->sk) * sizeof(TileRange));
+}
+
+int ringattn_fused_fwd(const ra_problem* p, int n_blocks, const void* q, const void* const* k_blocks,
+                       const void* const* v_blocks, float* lse, void* out, const int32_t* q_pos,
+                       const int32_t* const* kv_pos, const int32_t* q_doc, const int32_t* const* kv_doc,
+                       int mask_mode, int flags, void* workspace, size_t workspace_bytes, void* stream) {
+  if (int rc = check_problem(p)) return rc;
+  if (n_blocks < 1 || n_blocks > RA_FUSED_MAX_BLOCKS)
+    return fail(RA_ERR_INVALID, "n_blocks = %d outside [1, %d]", n_blocks, RA_FUSED_MAX_BLOCKS);
+  if (p->dtype != RA_BF16) return fail(RA_ERR_UNSUPPORTED, "the fused forward is bf16 only");
+  if (flags & ~RA_NO_SKIP) return fail(RA_ERR_INVALID, "unknown fused flags 0x%x", flags);
+  if (!k_blocks || !v_blocks || !kv_pos) return fail(RA_ERR_INVALID, "k_blocks, v_blocks and kv_pos are required");
+  const bool doc = mask_mode == RA_MASK_DOC_CAUSAL;
+  if (doc && !kv_doc) return fail(RA_ERR_INVALID, "kv_doc is required for DOC_CAUSAL");
+  for (int j = 0; j < n_blocks; ++j)
+    if (int rc = check_mask(mask_mode, q_doc, doc ? kv_doc[j] : nullptr, p->sk > 0)) return rc;
+  if (p->sq == 0) return ok();
+  if (int rc = check_ptr(q, "q")) return rc;
+  if (int rc = check_ptr(lse, "lse", 4)) return rc;
+  if (int rc = check_ptr(out, "out")) return rc;
+  if (int rc = check_ptr(q_pos, "q_pos", 4)) return rc;
+  if (p->sk > 0) {
+    for (int j = 0; j < n_blocks; ++j) {
+      if (int rc = check_ptr(k_blocks[j], "k_blocks[j]")) return rc;
+      if (int rc = check_ptr(v_blocks[j], "v_blocks[j]")) return rc;
+      if (int rc = check_ptr(kv_pos[j], "kv_pos[j]", 4)) return rc;
+    }
+  }
+  const size_t need = ringattn_fused_workspace_size(p, n_blocks);
+  if (workspace_bytes < need || (need && !workspace))
+    return fail(RA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, workspace_bytes);
+  if (!aligned(workspace, 16)) return fail(RA_ERR_INVALID, "workspace is not 16-byte aligned");
+
+  hipStream_t st = (hipStream_t)stream;
+  char* base = (char*)workspace;
+  TileRange* tq = (TileRange*)base;
+  base += align256((size_t)n_tiles(p->sq) * sizeof(TileRange));
+  const size_t kv_bytes = align256((size_t)n_tiles(p->sk) * sizeof(TileRange));
+  hipError_t e = launch_tile_ranges(q_pos, doc ? q_doc : nullptr, p->sq, tq, st);
+  for (int j = 0; j < n_blocks && e == hipSuccess && p->sk > 0; ++j)
+    e = launch_tile_ranges(kv_pos[j], doc ? kv_doc[j] : nullptr, p->sk, (TileRange*)(base + j * kv_bytes), st);
+  if (e != hipSuccess) return hip_fail(e, "tile-range kernel launch");
+  FwdArgs a = make_fwd(p, q, p->sk > 0 ? k_blocks[0] : nullptr, p->sk > 0 ? v_blocks[0] : nullptr, nullptr, lse, out,
+                       q_pos, p->sk > 0 ? kv_pos[0] : nullptr, q_doc, doc ? kv_doc[0] : nullptr, tq,
+                       (TileRange*)base, mask_mode, flags | RA_STEP_FIRST | RA_STEP_LAST);
+  a.n_blocks = n_blocks;
+  for (int j = 0; j < n_blocks && p->sk > 0; ++j) {
+    a.kb[j] = k_blocks[j];
+    a.vb[j] = v_blocks[j];
+    a.kposb[j] = kv_pos[j];
+    a.kdocb[j] = doc ? kv_doc[j] : nullptr;
+    a.ktilesb[j] = (const TileRange*)(base + j * kv_bytes);
+  }
+  e = launch_fwd_bf16(a, p->head_dim, st);
+  if (e != hipSuccess) return hip_fail(e, "fused forward kernel launch");
   return ok();
 }
 
@@ -331,7 +398,8 @@ RunLayout run_layout(const ra_run_desc* d) {
   return L;
 }
 
-const int kRunFlags = RA_NO_SKIP | RA_RUN_SERIAL_COPY | RA_RUN_POISON | RA_RUN_MERGE_KERNEL | RA_RUN_COPY_ENGINE;
+const int kRunFlags = RA_NO_SKIP | RA_RUN_SERIAL_COPY | RA_RUN_POISON | RA_RUN_MERGE_KERNEL | RA_RUN_COPY_ENGINE |
+                      RA_RUN_ALLGATHER;
 
 int check_run(const ra_run_desc* d) {
   if (!d) return fail(RA_ERR_INVALID, "run descriptor is NULL");
@@ -345,6 +413,14 @@ int check_run(const ra_run_desc* d) {
   if (stop <= d->start_step || stop > d->n_ranks) return fail(RA_ERR_INVALID, "stop_step out of range");
   if (d->pass != RA_PASS_FWD && d->pass != RA_PASS_BWD) return fail(RA_ERR_INVALID, "pass must be 1 or 2");
   if (d->flags & ~kRunFlags) return fail(RA_ERR_INVALID, "unknown run flags 0x%x", d->flags);
+  if (d->flags & RA_RUN_ALLGATHER) {
+    if (d->pass != RA_PASS_FWD) return fail(RA_ERR_INVALID, "RA_RUN_ALLGATHER is a forward-pass mode");
+    if (d->prob.dtype != RA_BF16) return fail(RA_ERR_UNSUPPORTED, "RA_RUN_ALLGATHER is bf16 only");
+    if (d->n_ranks > RA_FUSED_MAX_BLOCKS)
+      return fail(RA_ERR_UNSUPPORTED, "RA_RUN_ALLGATHER takes at most %d ranks", RA_FUSED_MAX_BLOCKS);
+    if (d->start_step != 0 || (d->stop_step != 0 && d->stop_step != d->n_ranks))
+      return fail(RA_ERR_INVALID, "RA_RUN_ALLGATHER runs the whole ring (start_step 0, stop_step n_ranks)");
+  }
   const ra_problem* p = &d->prob;
   const int64_t* s = p->kv_stride;
   const int64_t span = (int64_t)(p->batch - 1) * s[0] + (int64_t)(p->hkv - 1) * s[1] + (int64_t)(p->sk - 1) * s[2] +
@@ -394,7 +470,9 @@ extern "C" int ringattn_run(const ra_run_desc* d, const void* const* q, const vo
   // ---- host-side validation of every pointer the selected pass uses ----
   if (!q || !k_home || !v_home || !q_pos || !kv_pos) return fail(RA_ERR_INVALID, "q, k_home, v_home, q_pos and kv_pos arrays are required");
   if (doc && (!q_doc || !kv_doc)) return fail(RA_ERR_INVALID, "doc-causal mask needs q_doc and kv_doc arrays");
-  if (fwd && (!o_acc || !lse)) return fail(RA_ERR_INVALID, "forward needs o_acc and lse arrays");
+  const bool allgather = (d->flags & RA_RUN_ALLGATHER) != 0;
+  if (fwd && !allgather && (!o_acc || !lse)) return fail(RA_ERR_INVALID, "forward needs o_acc and lse arrays");
+  if (allgather && (!lse || !out)) return fail(RA_ERR_INVALID, "all-gather mode needs lse and out arrays");
   if (!fwd && (!lse || !out || !d_o || !delta || !dq || !dk || !dv))
     return fail(RA_ERR_INVALID, "backward needs lse, out, d_o, delta, dq, dk and dv arrays");
   char name[64];
@@ -409,7 +487,10 @@ extern "C" int ringattn_run(const ra_run_desc* d, const void* const* q, const vo
     }
     snprintf(name, sizeof name, "lse[%d]", i);
     if (int rc = check_ptr(lse[i], name, 4)) return rc;
-    if (fwd) {
+    if (fwd && allgather) {
+      snprintf(name, sizeof name, "out[%d]", i);
+      if (int rc = check_ptr(out[i], name)) return rc;
+    } else if (fwd) {
       snprintf(name, sizeof name, "o_acc[%d]", i);
       if (int rc = check_ptr(o_acc[i], name)) return rc;
       if (out && out[i] && !aligned(out[i], 16)) return fail(RA_ERR_INVALID, "out[%d] is not 16-byte aligned", i);
@@ -494,8 +575,29 @@ extern "C" int ringattn_run(const ra_run_desc* d, const void* const* q, const vo
       if ((e = launch_bwd_preprocess(p->batch, p->hq, p->sq, p->head_dim, out[i], d_o[i], strides3(p->q_stride),
                                      p->dtype, delta[i], cs)) != hipSuccess)
         return hip_fail(e, "backward preprocess kernel launch");
-  if (!serial) {
-    // the tile tables are written on the compute stream; they are read only there, so no wait is needed
+  if (allgather) {
+    // every block is resident: one launch per emulated rank over all of them, in ring order
+    if (d->step_events && d->step_events[0] && (e = hipEventRecord((hipEvent_t)d->step_events[0], cs)) != hipSuccess)
+      return hip_fail(e, "hipEventRecord (step_events)");
+    for (int i = 0; i < R; ++i) {
+      const int n0 = block_of(i, 0);
+      FwdArgs a = make_fwd(p, q[i], k_home[n0], v_home[n0], nullptr, lse[i], out[i], q_pos[i], kv_pos[n0],
+                           doc ? q_doc[i] : nullptr, doc ? kv_doc[n0] : nullptr, qtab(i), kvtab(n0), mask,
+                           step_flags_extra | RA_STEP_FIRST | RA_STEP_LAST);
+      a.n_blocks = N;
+      for (int t = 0; t < N; ++t) {
+        const int n = block_of(i, t);
+        a.kb[t] = k_home[n];
+        a.vb[t] = v_home[n];
+        a.kposb[t] = kv_pos[n];
+        a.kdocb[t] = doc ? kv_doc[n] : nullptr;
+        a.ktilesb[t] = kvtab(n);
+      }
+      if ((e = launch_fwd_bf16(a, p->head_dim, cs)) != hipSuccess) return hip_fail(e, "fused forward kernel launch");
+    }
+    if (d->step_events && d->step_events[1] && (e = hipEventRecord((hipEvent_t)d->step_events[1], cs)) != hipSuccess)
+      return hip_fail(e, "hipEventRecord (step_events)");
+    return ok();
   }
 
   // Copy block (rank - t) of every emulated rank into slot t & 1.

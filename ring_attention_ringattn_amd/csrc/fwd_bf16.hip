@@ -48,6 +48,11 @@
 // The step's normalised partial (O_t = acc / l, LSE_t = m ln2 + ln l) is
 // merged into the running (o_acc, lse) in the epilogue with the exact
 // log-sum-exp combine; FIRST overwrites, LAST also writes bf16 `out`.
+//
+// All-gather mode: one launch may take up to MAX_FUSED_BLOCKS resident K/V
+// blocks; the tile list then spans every block (entries carry the block
+// index) and the softmax state stays in registers across blocks, so there is
+// no running output between blocks (the launch is FIRST | LAST).
 #include "mfma_tile.h"
 
 namespace ra {
@@ -138,10 +143,10 @@ __global__ __launch_bounds__(NWAVES * 64, 1) void fwd_bf16_kernel(FwdArgs a) {
 #pragma unroll
   for (int db = 0; db < D / 32; ++db) acc[db] = f32x16{};
 
-  const __bf16* kptr = (const __bf16*)a.k + b * a.kvs.b + kvh * a.kvs.h;
-  const __bf16* vptr = (const __bf16*)a.v + b * a.kvs.b + kvh * a.kvs.h;
+  const size_t kvoff = b * a.kvs.b + kvh * a.kvs.h;   // this (batch, kv head) within a block
   const int rsb = (int)(a.kvs.s * 2);   // bytes between consecutive keys
-  const int nkt = n_tiles(a.sk);
+  const int nkt = n_tiles(a.sk);        // tiles per block
+  const int ntot = nkt * a.n_blocks;    // tiles over all blocks (list index space)
   const bool no_skip = (a.flags & FLAG_NO_SKIP) != 0;
   const float sl2 = a.scale_log2;
   const bool no_causal = mask == MASK_NONE, no_doc = mask != MASK_DOC_CAUSAL;
@@ -155,26 +160,27 @@ __global__ __launch_bounds__(NWAVES * 64, 1) void fwd_bf16_kernel(FwdArgs a) {
   for (int c = 0; c < C::CPW; ++c) voff[c] = chunk_voff<D>(c * NWAVES + wave, lane, rsb);
 
   // Start streaming the K rows (with the key positions and documents, wave 0)
-  // / the V rows of the tile at list entry li into buffer li % NBUF.  Every
-  // wave issues its share; keys past the end of the block read as zero.
-  auto issue_k = [&] __device__(int li, int tile) {
-    const int buf = li % NBUF;
+  // / the V rows of the tile of list position li (entry ent: tile | block << 12)
+  // into buffer li % NBUF.  Every wave issues its share; keys past the end of
+  // the block read as zero.
+  auto issue_k = [&] __device__(int li, int ent) {
+    const int buf = li % NBUF, tile = ent & 0xfff, blk = (ent >> 12) & 0xf;
     const int kbase = tile * BN;
     const int rows = min(BN, a.sk - kbase);
     if (wave == 0) {
-      dma4(a.kv_pos + kbase, rows * 4, (RA_LDS void*)&kvp[buf][0], lane * 4);
-      if (mask == MASK_DOC_CAUSAL) dma4(a.kv_doc + kbase, rows * 4, (RA_LDS void*)&kvd[buf][0], lane * 4);
+      dma4(a.kposb[blk] + kbase, rows * 4, (RA_LDS void*)&kvp[buf][0], lane * 4);
+      if (mask == MASK_DOC_CAUSAL) dma4(a.kdocb[blk] + kbase, rows * 4, (RA_LDS void*)&kvd[buf][0], lane * 4);
     }
-    const __bf16* kb = kptr + (size_t)kbase * a.kvs.s;
+    const __bf16* kb = (const __bf16*)a.kb[blk] + kvoff + (size_t)kbase * a.kvs.s;
 #pragma unroll
     for (int c = 0; c < C::CPW; ++c)
       dma16(kb, rows * rsb, (RA_LDS void*)&Ks[buf][(c * NWAVES + wave) * 512], voff[c]);
   };
-  auto issue_v = [&] __device__(int li, int tile) {
-    const int buf = li % NBUF;
+  auto issue_v = [&] __device__(int li, int ent) {
+    const int buf = li % NBUF, tile = ent & 0xfff, blk = (ent >> 12) & 0xf;
     const int kbase = tile * BN;
     const int rows = min(BN, a.sk - kbase);
-    const __bf16* vb = vptr + (size_t)kbase * a.kvs.s;
+    const __bf16* vb = (const __bf16*)a.vb[blk] + kvoff + (size_t)kbase * a.kvs.s;
 #pragma unroll
     for (int c = 0; c < C::CPW; ++c)
       dma16(vb, rows * rsb, (RA_LDS void*)&Vs[buf][(c * NWAVES + wave) * 512], voff[c]);
@@ -209,7 +215,7 @@ __global__ __launch_bounds__(NWAVES * 64, 1) void fwd_bf16_kernel(FwdArgs a) {
   // lane (g, j), value v of block mb holds key mb*32 + 16*(v/8) + 8*g + v%8 for query j.
   auto softmax = [&] __device__(int ent, int buf, f32x16(&s)[2], bf16x8(&pf)[4]) {
     const bool partial = (ent >> 24) == TILE_PARTIAL;
-    const int kvalid = a.sk - (ent & 0xffffff) * BN;   // keys of this tile that exist (>= BN: all)
+    const int kvalid = a.sk - (ent & 0xfff) * BN;   // keys of this tile that exist (>= BN: all)
     if (partial) {
       asm volatile("" ::: "memory");   // keep this a real branch: full tiles must not pay for masking
 #pragma unroll
@@ -278,12 +284,15 @@ __global__ __launch_bounds__(NWAVES * 64, 1) void fwd_bf16_kernel(FwdArgs a) {
 
   f32x16 s[2];
   bf16x8 pf[4];
-  for (int c0 = 0; c0 < nkt; c0 += LIST) {
+  for (int c0 = 0; c0 < ntot; c0 += LIST) {
     // ---- compact the non-empty tiles of this chunk into `list` ----
     const int t = c0 + tid;
     int cls = TILE_EMPTY;
-    if (t < nkt) {
-      cls = classify(qr, a.kv_tiles[t], (t + 1) * TILE <= a.sk, mask);
+    int tl = 0, blk = 0;
+    if (t < ntot) {
+      blk = t / nkt;
+      tl = t - blk * nkt;
+      cls = classify(qr, a.ktilesb[blk][tl], (tl + 1) * TILE <= a.sk, mask);
       if (no_skip && cls == TILE_EMPTY) cls = TILE_PARTIAL;
     }
     const unsigned long long bal = __ballot(cls != TILE_EMPTY);
@@ -297,11 +306,11 @@ __global__ __launch_bounds__(NWAVES * 64, 1) void fwd_bf16_kernel(FwdArgs a) {
       off += (w < wave) ? c : 0;
       total += c;
     }
-    if (cls != TILE_EMPTY) list[off + my] = t | (cls << 24);
+    if (cls != TILE_EMPTY) list[off + my] = tl | (blk << 12) | (cls << 24);
     __syncthreads();
     total = __builtin_amdgcn_readfirstlane(total);
     if (total == 0) continue;
-    auto tile_of = [&] __device__(int li) { return __builtin_amdgcn_readfirstlane(list[li]) & 0xffffff; };
+    auto tile_of = [&] __device__(int li) { return __builtin_amdgcn_readfirstlane(list[li]) & 0xffff; };
 
     // prologue: K(0..2), V(0..1); V(-1) := 0 and P := 0 so that period 0's PV adds nothing
     for (int t = 0; t < min(3, total); ++t) issue_k(t, tile_of(t));
@@ -327,8 +336,8 @@ __global__ __launch_bounds__(NWAVES * 64, 1) void fwd_bf16_kernel(FwdArgs a) {
       // list entries used in this phase: one LDS round trip for all three
       const int e0 = list[min(i, LIST - 1)], e2 = list[min(i + 2, LIST - 1)], e3 = list[min(i + 3, LIST - 1)];
       // list entries are workgroup-uniform: keep them scalar so the branches on them stay branches
-      if (i + 3 < total) issue_k(i + 3, __builtin_amdgcn_readfirstlane(e3) & 0xffffff);
-      if (i + 2 < total) issue_v(i + 2, __builtin_amdgcn_readfirstlane(e2) & 0xffffff);
+      if (i + 3 < total) issue_k(i + 3, __builtin_amdgcn_readfirstlane(e3) & 0xffff);
+      if (i + 2 < total) issue_v(i + 2, __builtin_amdgcn_readfirstlane(e2) & 0xffff);
       if (i < total) softmax(__builtin_amdgcn_readfirstlane(e0), i % NBUF, s, pf);
       __syncthreads();
     }
@@ -350,7 +359,7 @@ __global__ __launch_bounds__(NWAVES * 64, 1) void fwd_bf16_kernel(FwdArgs a) {
     w_p = wp;
     w_t = wt * inv;
   }
-  float* op = a.o_acc + orow * D;
+  float* op = a.o_acc ? a.o_acc + orow * D : nullptr;   // null: fused launch, out and lse only
   __bf16* outp = last ? (__bf16*)a.out + b * a.qs.b + h * a.qs.h + qrow * a.qs.s : nullptr;
 #pragma unroll
   for (int db = 0; db < D / 32; ++db) {
@@ -360,7 +369,7 @@ __global__ __launch_bounds__(NWAVES * 64, 1) void fwd_bf16_kernel(FwdArgs a) {
       f32x4 o = {acc[db][vh * 4 + 0] * w_t, acc[db][vh * 4 + 1] * w_t, acc[db][vh * 4 + 2] * w_t,
                  acc[db][vh * 4 + 3] * w_t};
       if (!first) o += w_p * *(const f32x4*)(op + d);
-      *(f32x4*)(op + d) = o;
+      if (op) *(f32x4*)(op + d) = o;
       if (last) {
         bf16x4 ob = {(__bf16)o[0], (__bf16)o[1], (__bf16)o[2], (__bf16)o[3]};
         *(bf16x4*)(outp + d) = ob;

@@ -27,9 +27,11 @@ struct Strides {
   int64_t b, h, s;
 };
 
+constexpr int MAX_FUSED_BLOCKS = 16;   // K/V blocks one fused (all-gather) forward launch can take
+
 struct FwdArgs {
   const void* q;
-  const void* k;
+  const void* k;      // block 0 (the only block of a ring step)
   const void* v;
   float* o_acc;       // dense [B][Hq][Sq][D]
   float* lse;         // dense [B][Hq][Sq]
@@ -46,6 +48,15 @@ struct FwdArgs {
   float scale_log2;   // softmax scale * log2(e)
   int mask;
   int flags;
+  // Fused (all-gather) forward: n_blocks K/V blocks of sk keys each, same strides;
+  // entry 0 repeats k, v, kv_pos, kv_doc, kv_tiles.  A ring step has n_blocks = 1.
+  // o_acc may be null for a fused launch (FIRST | LAST: out and lse only).
+  int n_blocks;
+  const void* kb[MAX_FUSED_BLOCKS];
+  const void* vb[MAX_FUSED_BLOCKS];
+  const int* kposb[MAX_FUSED_BLOCKS];
+  const int* kdocb[MAX_FUSED_BLOCKS];
+  const TileRange* ktilesb[MAX_FUSED_BLOCKS];
 };
 
 struct BwdArgs {

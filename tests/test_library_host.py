@@ -22,12 +22,12 @@ def declared_functions():
 
 def test_header_exports_match_library():
     names = declared_functions()
-    assert len(names) == 10, names
+    assert len(names) == 12, names
     assert sorted(_lib.EXPORTS) == names
     lib = _lib.load()
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.ringattn_version() == 1
+    assert lib.ringattn_version() == 2
 
 
 def _problem(**kw):
@@ -99,6 +99,55 @@ def test_step_fwd_validation(name, p, kw, ptr, status):
     assert h.untouched()
 
 
+def fused_fwd(h, p, n_blocks=2, mask=1, flags=0, ws_bytes=1 << 20, **ptr):
+    pp = ctypes.POINTER(ctypes.c_void_p)
+    arrs = []
+
+    def arr(name, n):
+        if name is None:
+            return None
+        a = (ctypes.c_void_p * max(n, 1))(*[h.bufs[name].ctypes.data] * max(n, 1))
+        arrs.append(a)
+        return ctypes.cast(a, pp)
+    args = dict(q=h.p("q"), k=arr("k", n_blocks), v=arr("v", n_blocks), lse=h.p("lse"), out=h.p("out"),
+                qp=h.p("qp"), kp=arr("kp", n_blocks), qd=None, kd=None, ws=h.p("ws"))
+    args.update(ptr)
+    return _lib.load().ringattn_fused_fwd(ctypes.byref(p), n_blocks, args["q"], args["k"], args["v"], args["lse"],
+                                          args["out"], args["qp"], args["kp"], args["qd"], args["kd"], mask, flags,
+                                          args["ws"], ws_bytes, None)
+
+
+FUSED_CASES = [
+    ("no blocks", _problem(), {"n_blocks": 0}, {}, _lib.RA_ERR_INVALID),
+    ("too many blocks", _problem(), {"n_blocks": _lib.RA_FUSED_MAX_BLOCKS + 1}, {}, _lib.RA_ERR_INVALID),
+    ("fp32 problem", _problem(dtype=_lib.RA_F32), {}, {}, _lib.RA_ERR_UNSUPPORTED),
+    ("step flag", _problem(), {"flags": _lib.RA_STEP_FIRST}, {}, _lib.RA_ERR_INVALID),
+    ("null block array", _problem(), {}, {"k": None}, _lib.RA_ERR_INVALID),
+    ("null out", _problem(), {}, {"out": None}, _lib.RA_ERR_INVALID),
+    ("doc mask without docs", _problem(), {"mask": 2}, {}, _lib.RA_ERR_INVALID),
+    ("workspace too small", _problem(), {"ws_bytes": 16}, {}, _lib.RA_ERR_WORKSPACE),
+]
+
+
+@pytest.mark.parametrize("name,p,kw,ptr,status", FUSED_CASES, ids=[c[0] for c in FUSED_CASES])
+def test_fused_fwd_validation(name, p, kw, ptr, status):
+    h = Host()
+    rc = fused_fwd(h, p, **kw, **ptr)
+    assert rc == status, _lib.load().ringattn_last_error()
+    assert _lib.load().ringattn_last_error()
+    assert h.untouched()
+
+
+def test_fused_workspace_size():
+    lib = _lib.load()
+    p = _problem(sq=1000, sk=130)
+    one = lib.ringattn_fused_workspace_size(ctypes.byref(p), 1)
+    four = lib.ringattn_fused_workspace_size(ctypes.byref(p), 4)
+    assert one >= (16 + 3) * 16 and four - one == 3 * 256      # 3 more tile tables of 3 tiles (256-aligned)
+    assert lib.ringattn_fused_workspace_size(ctypes.byref(p), 0) == 0
+    assert lib.ringattn_fused_workspace_size(ctypes.byref(p), _lib.RA_FUSED_MAX_BLOCKS + 1) == 0
+
+
 def test_empty_query_shard_is_a_no_op():
     h = Host()
     assert step_fwd(h, _problem(sq=0)) == _lib.RA_OK
@@ -152,6 +201,28 @@ def test_run_validation(field, value, status):
     d.n_ranks, d.n_emulated, d.mask_mode, d.pass_ = 8, 1, 1, _lib.RA_PASS_FWD
     setattr(d, field, value)
     assert _run(h, d) == status, _lib.load().ringattn_last_error()
+    assert h.untouched()
+
+
+def test_run_allgather_mode_validation():
+    h = Host()
+    d = _lib.RaRunDesc()
+    d.prob = _problem()
+    d.n_ranks, d.n_emulated, d.mask_mode, d.pass_ = 8, 1, 1, _lib.RA_PASS_FWD
+    d.flags = _lib.RA_RUN_ALLGATHER
+    d.pass_ = _lib.RA_PASS_BWD
+    assert _run(h, d) == _lib.RA_ERR_INVALID                    # forward-pass mode only
+    d.pass_ = _lib.RA_PASS_FWD
+    d.start_step = 1
+    assert _run(h, d) == _lib.RA_ERR_INVALID                    # the whole ring only
+    d.start_step = 0
+    d.prob = _problem(dtype=_lib.RA_F32)
+    assert _run(h, d) == _lib.RA_ERR_UNSUPPORTED                # bf16 only
+    d.prob = _problem()
+    d.n_ranks = _lib.RA_FUSED_MAX_BLOCKS + 1
+    assert _run(h, d) == _lib.RA_ERR_UNSUPPORTED                # at most 16 resident blocks
+    d.n_ranks = 8
+    assert _run(h, d, out=None) == _lib.RA_ERR_INVALID          # out is required (no o_acc is written)
     assert h.untouched()
 
 
