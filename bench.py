@@ -149,6 +149,14 @@ def run_fwd(s, side, events=None):
                     workspace=s["ws"], copy_stream=side, step_events=events)
 
 
+def run_fwd_allgather(s):
+    """The same share with every block resident: one fused launch over all N blocks (no ring)."""
+    import ring_attention_ringattn_amd as ra
+    ra.ringattn_run(s["q"], s["k"], s["v"], s["q_pos"], s["kv_pos"], lse=s["lse"], out=s["out"],
+                    q_doc=s["q_doc"], kv_doc=s["kv_doc"], first_rank=s["ranks"][0], mask_mode=s["mask"],
+                    workspace=s["ws"], flags=ra.RA_RUN_ALLGATHER)
+
+
 def run_bwd(s, side):
     import ring_attention_ringattn_amd as ra
     for t in s["dq"] + s["dk"] + s["dv"]:
@@ -296,10 +304,18 @@ def main():
                      "flop_per_launch": flops_step},
     }
 
+    # the all-gather rotation on the same share: every block resident, one fused launch
+    t_ag = timed(lambda: run_fwd_allgather(s), args.steps, args.warmup)
+    result["legs"] = {"fwd_allgather_131072_rank_share": {
+        "workload": "the same rank share with all 8 K/V blocks resident (all-gather rotation): one fused "
+                    "launch over every block, softmax state kept in registers, no ring steps",
+        "fwd_ms": round(t_ag * 1e3, 3), "fwd_tflops": round(flops_ring / t_ag / 1e12, 2),
+        "pct_peak": round(100.0 * flops_ring / t_ag / 1e12 / PEAK_BF16_TFLOPS, 2)}}
+
     if not args.no_bwd:
         del s
         torch.cuda.empty_cache()
-        result["legs"] = {
+        result["legs"].update({
             "fwd_bwd_262144_rank_share": fwd_bwd_leg(
                 "c4", [args.rank], side, args.steps, args.warmup,
                 "rank share of a 262144-token causal context over 8 zigzag shards (32768 local queries, "
@@ -308,7 +324,7 @@ def main():
                 "c5", [0, 1, 2, 3], side, args.steps, args.warmup,
                 "65536 packed tokens of lognormal documents (seed 5: 22 documents), document-causal, "
                 "4 contiguous ring shards, all ranks, 32/8 heads, D=128, bf16, forward + backward"),
-        }
+        })
 
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(*host, args.cpu_budget)

@@ -1,0 +1,124 @@
+"""HIP-graph capture of the ring driver: a captured ringattn_run replays to the eager result.
+
+The forward ring (side-stream staging copies ordered by events) and the
+backward ring are captured once each; every replay, with unrelated eager work
+and a poisoning of the outputs between replays, must reproduce the eager run
+bit for bit (same kernels, same inputs, same schedule).
+"""
+import pytest
+import torch
+
+import ring_attention_ringattn_amd as ra
+import synthetic
+from tests.gpu_util import dev, print_case
+
+pytestmark = pytest.mark.gpu
+
+BF = torch.bfloat16
+
+
+def _share():
+    w = synthetic.small_workload("c2", seq=4096, n_shards=4, hq=8, hkv=2, seed=33)
+    inp = synthetic.make_inputs(w, backward=True)
+    pos = ra.sharding.shard_positions(w.seq, 4, "zigzag")
+    s = {"q": [dev(inp["q"][:, :, p], BF) for p in pos], "k": [dev(inp["k"][:, :, p], BF) for p in pos],
+         "v": [dev(inp["v"][:, :, p], BF) for p in pos], "do": [dev(inp["do"][:, :, p], BF) for p in pos],
+         "qp": [dev(p, torch.int32) for p in pos]}
+    s["o_acc"] = [torch.empty(x.shape, device="cuda") for x in s["q"]]
+    s["lse"] = [torch.empty(x.shape[:3], device="cuda") for x in s["q"]]
+    s["out"] = [torch.empty_like(x) for x in s["q"]]
+    s["delta"] = [torch.empty(x.shape[:3], device="cuda") for x in s["q"]]
+    s["dq"] = [torch.empty(x.shape, device="cuda") for x in s["q"]]
+    s["dk"] = [torch.empty(x.shape, device="cuda") for x in s["k"]]
+    s["dv"] = [torch.empty(x.shape, device="cuda") for x in s["k"]]
+    s["ws"] = torch.empty(ra.ringattn_run_workspace_size(s["q"][0], s["k"][0], 4, 4, pass_=ra.RA_PASS_BWD),
+                          dtype=torch.uint8, device="cuda")
+    return s
+
+
+def _fwd(s, side):
+    ra.ringattn_run(s["q"], s["k"], s["v"], s["qp"], s["qp"], o_acc=s["o_acc"], lse=s["lse"], out=s["out"],
+                    workspace=s["ws"], copy_stream=side)
+
+
+def _bwd(s, side):
+    for t in s["dq"] + s["dk"] + s["dv"]:
+        t.zero_()          # a fill kernel, not a memset node
+    ra.ringattn_run(s["q"], s["k"], s["v"], s["qp"], s["qp"], lse=s["lse"], out=s["out"], d_o=s["do"],
+                    delta=s["delta"], dq=s["dq"], dk=s["dk"], dv=s["dv"], pass_=ra.RA_PASS_BWD, workspace=s["ws"],
+                    copy_stream=side)
+
+
+def _snapshot(ts):
+    return [t.clone() for t in ts]
+
+
+def _poison(ts):
+    for t in ts:
+        t.fill_(float("nan"))
+
+
+def _replay_matches(graph, outs, ref):
+    a = torch.randn(512, 512, device="cuda")
+    for rep in range(3):
+        _poison(outs)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for got, want in zip(outs, ref):
+            assert torch.equal(got, want), f"replay {rep} differs from the eager run"
+        (a @ a).sum().item()            # unrelated eager work between replays
+        torch.cuda.synchronize()
+
+
+def test_forward_ring_graph_replays_bitwise():
+    print_case("graph: forward ring, 4 emulated ranks, side-stream staging copies")
+    s = _share()
+    side = torch.cuda.Stream()
+    _fwd(s, side)
+    torch.cuda.synchronize()
+    outs = s["o_acc"] + s["lse"] + s["out"]
+    ref = _snapshot(outs)
+    cap = torch.cuda.Stream()
+    cap.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=cap):
+        _fwd(s, side)
+    torch.cuda.synchronize()
+    _replay_matches(g, outs, ref)
+
+
+def test_backward_ring_graph_replays_bitwise():
+    print_case("graph: backward ring, 4 emulated ranks")
+    s = _share()
+    side = torch.cuda.Stream()
+    _fwd(s, side)
+    _bwd(s, side)
+    torch.cuda.synchronize()
+    outs = s["dq"] + s["dk"] + s["dv"] + s["delta"]
+    ref = _snapshot(outs)
+    cap = torch.cuda.Stream()
+    cap.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=cap):
+        _bwd(s, side)
+    torch.cuda.synchronize()
+    _replay_matches(g, outs, ref)
+
+
+def test_allgather_forward_graph_replays_bitwise():
+    print_case("graph: all-gather forward, 4 emulated ranks")
+    s = _share()
+    run = lambda: ra.ringattn_run(s["q"], s["k"], s["v"], s["qp"], s["qp"], lse=s["lse"], out=s["out"],
+                                  workspace=s["ws"], flags=ra.RA_RUN_ALLGATHER)
+    run()
+    torch.cuda.synchronize()
+    outs = s["lse"] + s["out"]
+    ref = _snapshot(outs)
+    cap = torch.cuda.Stream()
+    cap.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=cap):
+        run()
+    torch.cuda.synchronize()
+    _replay_matches(g, outs, ref)
