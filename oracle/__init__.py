@@ -11,6 +11,9 @@ arithmetic.
   LSE, and its backward, in fp64 (pinned by tests/test_oracle_pins.py).
 * ``ring``: the ring method emulated in fp64 (shards, circulating blocks,
   exact LSE merge); pinned against ``attention`` to 1e-12.
+* ``dynamic_cp``: exhaustive Dynamic-CP planner for small instances (the
+  optimum the product's heuristic solver is checked against); pinned by a
+  hand-checked case in tests/test_dynamic_cp.py.
 
 Every function is pinned by a test against closed forms, invariants, a
 50-digit Decimal brute force or finite differences; none is "parity

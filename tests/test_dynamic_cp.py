@@ -1,0 +1,79 @@
+"""Dynamic-CP cost model and solver (host): fit, plan constraints, and the heuristic against
+the exhaustive optimum of oracle/dynamic_cp.py on small instances."""
+import numpy as np
+import pytest
+
+from oracle.dynamic_cp import optimal_time
+from ring_attention_ringattn_amd import dynamic_cp as dcp
+
+MODEL = dcp.CostModel(alpha=2e-8, beta=1e-4, eps=2e-6, gamma=0.05, delta=0.1)
+
+
+def _cost(docs, c):
+    # the same cost form, written out independently for the oracle
+    return (2e-8 * sum(x * x for x in docs) + 1e-4 * sum(docs)) / c + 2e-6 * sum(docs) + 0.05 * c + 0.1
+
+
+def test_fit_recovers_a_known_model():
+    rng = np.random.default_rng(0)
+    samples = []
+    for tot in (8192, 16384, 32768, 65536):
+        for dl in (256, 1024, 4096, 16384):
+            if dl <= tot:
+                for c in (1, 2, 4, 8):
+                    docs = [dl] * (tot // dl)
+                    samples.append((docs, c, MODEL.predict(docs, c) * (1 + 1e-4 * rng.standard_normal())))
+    fit, err = dcp.fit_cost_model(samples)
+    assert err < 1e-3
+    for name in ("alpha", "beta", "eps", "gamma", "delta"):
+        assert getattr(fit, name) == pytest.approx(getattr(MODEL, name), rel=2e-2)
+
+
+def test_cp_needed_is_the_smallest_power_of_two():
+    assert [dcp.cp_needed(n, 1000, 8) for n in (1, 1000, 1001, 2000, 2001, 8000)] == [1, 1, 2, 2, 4, 8]
+    with pytest.raises(ValueError):
+        dcp.cp_needed(8001, 1000, 8)
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_plans_respect_every_constraint(seed):
+    lengths = dcp.lognormal_lengths(seed, 200)
+    for solve in (dcp.solve_dynamic, dcp.solve_static):
+        plan = solve(lengths, 8, 16384, MODEL)
+        dcp.check_plan(plan, lengths, 8, 16384)
+        # the per-GPU loads are what the micro-batches charge
+        loads = [0.0] * 8
+        for mb in plan.micro_batches:
+            t = MODEL.predict([lengths[i] for i in mb.seqs], mb.cp)
+            for g in range(mb.group * mb.cp, (mb.group + 1) * mb.cp):
+                loads[g] += t
+        assert np.allclose(loads, plan.loads)
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_heuristic_near_the_exhaustive_optimum(seed):
+    rng = np.random.default_rng(100 + seed)
+    n = int(rng.integers(3, 6))
+    lengths = [int(x) for x in rng.integers(200, 4000, n)]
+    opt = optimal_time(lengths, 4, 2048, _cost)
+    got = dcp.solve_dynamic(lengths, 4, 2048, MODEL).time
+    assert opt <= got + 1e-9                    # the oracle really is a lower bound
+    assert got <= 1.5 * opt, (lengths, got, opt)
+
+
+def test_oracle_on_a_hand_checked_case():
+    # two sequences of 1500 tokens, 2 GPUs of 1000 tokens: each needs CP 2 and both share the
+    # GPUs, so the best iteration runs them one after the other on both GPUs
+    t = optimal_time([1500, 1500], 2, 1000, _cost)
+    assert t == pytest.approx(2 * _cost([1500], 2))
+    # one GPU of 4096 tokens: packing both into one micro-batch saves a fixed cost
+    t = optimal_time([1000, 2000], 1, 4096, _cost)
+    assert t == pytest.approx(_cost([1000, 2000], 1))
+
+
+def test_dynamic_beats_static_packing_on_lognormal_batches():
+    for seed in range(4):
+        lengths = dcp.lognormal_lengths(seed, 256)
+        dyn = dcp.solve_dynamic(lengths, 8, 16384, MODEL).time
+        sta = dcp.solve_static(lengths, 8, 16384, MODEL).time
+        assert dyn < sta
