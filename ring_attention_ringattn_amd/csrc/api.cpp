@@ -109,6 +109,17 @@ size_t step_ws(int sq, int sk) {
   return align256((size_t)n_tiles(sq) * sizeof(TileRange)) + align256((size_t)n_tiles(sk) * sizeof(TileRange));
 }
 
+// The bf16 forward reads each value block transposed (vt_transpose): room for one.
+size_t vt_ws(const ra_problem* p) {
+  return p->dtype == RA_BF16 ? align256(vt_block_bytes(p->batch, p->hkv, p->head_dim, p->sk)) : 0;
+}
+
+hipError_t transpose_v(const ra_problem* p, const void* v, void* vt, hipStream_t st) {
+  if (p->sk == 0) return hipSuccess;
+  return launch_vt_transpose(v, Strides{p->kv_stride[0], p->kv_stride[1], p->kv_stride[2]}, p->batch, p->hkv, p->sk,
+                             p->head_dim, vt, st);
+}
+
 struct StepTables {
   TileRange* q;
   TileRange* kv;
@@ -134,8 +145,9 @@ FwdArgs make_fwd(const ra_problem* p, const void* q, const void* k, const void* 
   a.scale_log2 = a.scale * 1.4426950408889634f;
   a.mask = mask; a.flags = flags;
   a.n_blocks = 1;
+  a.skp = vt_keys(p->sk);
   for (int j = 0; j < MAX_FUSED_BLOCKS; ++j) {
-    a.kb[j] = k; a.vb[j] = v; a.kposb[j] = kv_pos; a.kdocb[j] = kv_doc; a.ktilesb[j] = kt;
+    a.kb[j] = k; a.vb[j] = v; a.vtb[j] = v; a.kposb[j] = kv_pos; a.kdocb[j] = kv_doc; a.ktilesb[j] = kt;
   }
   return a;
 }
@@ -177,7 +189,7 @@ const char* ringattn_last_error(void) { return g_err.c_str(); }
 
 size_t ringattn_step_workspace_size(const ra_problem* p) {
   if (check_problem(p)) return 0;
-  return step_ws(p->sq, p->sk);
+  return step_ws(p->sq, p->sk) + vt_ws(p);
 }
 
 int ringattn_step_fwd(const ra_problem* p, const void* q, const void* k_blk, const void* v_blk, float* o_acc,
@@ -198,7 +210,7 @@ int ringattn_step_fwd(const ra_problem* p, const void* q, const void* k_blk, con
     if (int rc = check_ptr(kv_pos, "kv_pos", 4)) return rc;
   }
   if (out && !aligned(out, 16)) return fail(RA_ERR_INVALID, "out is not 16-byte aligned");
-  const size_t need = step_ws(p->sq, p->sk);
+  const size_t need = step_ws(p->sq, p->sk) + vt_ws(p);
   if (workspace_bytes < need || (need && !workspace))
     return fail(RA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, workspace_bytes);
   if (!aligned(workspace, 16)) return fail(RA_ERR_INVALID, "workspace is not 16-byte aligned");
@@ -210,6 +222,11 @@ int ringattn_step_fwd(const ra_problem* p, const void* q, const void* k_blk, con
   if (e == hipSuccess) e = launch_tile_ranges(kv_pos, doc ? kv_doc : nullptr, p->sk, t.kv, st);
   if (e != hipSuccess) return hip_fail(e, "tile-range kernel launch");
   FwdArgs a = make_fwd(p, q, k_blk, v_blk, o_acc, lse, out, q_pos, kv_pos, q_doc, kv_doc, t.q, t.kv, mask_mode, flags);
+  if (vt_ws(p)) {
+    void* vt = (char*)workspace + step_ws(p->sq, p->sk);
+    if ((e = transpose_v(p, v_blk, vt, st)) != hipSuccess) return hip_fail(e, "value transpose kernel launch");
+    a.vtb[0] = vt;
+  }
   e = enqueue_fwd(p, a, st);
   if (e != hipSuccess) return hip_fail(e, "forward step kernel launch");
   return ok();
@@ -219,7 +236,7 @@ size_t ringattn_fused_workspace_size(const ra_problem* p, int n_blocks) {
   if (check_problem(p)) return 0;
   if (n_blocks < 1 || n_blocks > RA_FUSED_MAX_BLOCKS) return 0;
   return align256((size_t)n_tiles(p->sq) * sizeof(TileRange)) +
-         (size_t)n_blocks * align256((size_t)n_tiles(p->sk) * sizeof(TileRange));
+         (size_t)n_blocks * (align256((size_t)n_tiles(p->sk) * sizeof(TileRange)) + vt_ws(p));
 }
 
 int ringattn_fused_fwd(const ra_problem* p, int n_blocks, const void* q, const void* const* k_blocks,
@@ -258,10 +275,14 @@ int ringattn_fused_fwd(const ra_problem* p, int n_blocks, const void* q, const v
   TileRange* tq = (TileRange*)base;
   base += align256((size_t)n_tiles(p->sq) * sizeof(TileRange));
   const size_t kv_bytes = align256((size_t)n_tiles(p->sk) * sizeof(TileRange));
+  char* vt_base = base + n_blocks * kv_bytes;
   hipError_t e = launch_tile_ranges(q_pos, doc ? q_doc : nullptr, p->sq, tq, st);
   for (int j = 0; j < n_blocks && e == hipSuccess && p->sk > 0; ++j)
     e = launch_tile_ranges(kv_pos[j], doc ? kv_doc[j] : nullptr, p->sk, (TileRange*)(base + j * kv_bytes), st);
   if (e != hipSuccess) return hip_fail(e, "tile-range kernel launch");
+  for (int j = 0; j < n_blocks && e == hipSuccess && p->sk > 0; ++j)
+    e = transpose_v(p, v_blocks[j], vt_base + j * vt_ws(p), st);
+  if (e != hipSuccess) return hip_fail(e, "value transpose kernel launch");
   FwdArgs a = make_fwd(p, q, p->sk > 0 ? k_blocks[0] : nullptr, p->sk > 0 ? v_blocks[0] : nullptr, nullptr, lse, out,
                        q_pos, p->sk > 0 ? kv_pos[0] : nullptr, q_doc, doc ? kv_doc[0] : nullptr, tq,
                        (TileRange*)base, mask_mode, flags | RA_STEP_FIRST | RA_STEP_LAST);
@@ -269,6 +290,7 @@ int ringattn_fused_fwd(const ra_problem* p, int n_blocks, const void* q, const v
   for (int j = 0; j < n_blocks && p->sk > 0; ++j) {
     a.kb[j] = k_blocks[j];
     a.vb[j] = v_blocks[j];
+    a.vtb[j] = vt_base + j * vt_ws(p);
     a.kposb[j] = kv_pos[j];
     a.kdocb[j] = doc ? kv_doc[j] : nullptr;
     a.ktilesb[j] = (const TileRange*)(base + j * kv_bytes);
@@ -366,6 +388,9 @@ namespace {
 struct RunLayout {
   size_t blk_elems;     // elements of one K (or V) block
   size_t blk_bytes;
+  bool vt;              // bf16 forward: value blocks circulate transposed
+  size_t vslot_bytes;   // one staged value block (V, or V^T when vt)
+  size_t off_vth;       // all-gather with vt: N transposed home value blocks
   size_t off_slots;     // 2 slots x R ranks x (K, V)
   size_t off_qtab;      // R q tables
   size_t off_kvtab;     // N kv tables
@@ -381,9 +406,16 @@ RunLayout run_layout(const ra_run_desc* d) {
   L.blk_bytes = align256(L.blk_elems * elem_size(p->dtype));
   L.qtab_bytes = align256((size_t)n_tiles(p->sq) * sizeof(TileRange));
   L.kvtab_bytes = align256((size_t)n_tiles(p->sk) * sizeof(TileRange));
+  L.vt = d->pass == RA_PASS_FWD && p->dtype == RA_BF16 && p->sk > 0;
+  L.vslot_bytes = L.vt ? vt_ws(p) : L.blk_bytes;
   size_t off = 0;
-  L.off_slots = off;
-  off += 2 * (size_t)d->n_emulated * 2 * L.blk_bytes;
+  L.off_vth = off;
+  if (L.vt && (d->flags & RA_RUN_ALLGATHER)) {
+    off += (size_t)d->n_ranks * L.vslot_bytes;   // every block resident: no staging slots
+  } else {
+    L.off_slots = off;
+    off += 2 * (size_t)d->n_emulated * (L.blk_bytes + L.vslot_bytes);
+  }
   L.off_qtab = off;
   off += (size_t)d->n_emulated * L.qtab_bytes;
   L.off_kvtab = off;
@@ -540,8 +572,10 @@ extern "C" int ringattn_run(const ra_run_desc* d, const void* const* q, const vo
                                                                     : hipMemcpyDeviceToDevice;
   const int step_flags_extra = d->flags & RA_NO_SKIP;
   char* ws = (char*)workspace;
-  auto slot_k = [&](int slot, int i) { return (void*)(ws + L.off_slots + ((size_t)(slot * R + i) * 2 + 0) * L.blk_bytes); };
-  auto slot_v = [&](int slot, int i) { return (void*)(ws + L.off_slots + ((size_t)(slot * R + i) * 2 + 1) * L.blk_bytes); };
+  auto slot_k = [&](int slot, int i) {
+    return (void*)(ws + L.off_slots + (size_t)(slot * R + i) * (L.blk_bytes + L.vslot_bytes));
+  };
+  auto slot_v = [&](int slot, int i) { return (void*)((char*)slot_k(slot, i) + L.blk_bytes); };
   auto qtab = [&](int i) { return (TileRange*)(ws + L.off_qtab + (size_t)i * L.qtab_bytes); };
   auto kvtab = [&](int n) { return (TileRange*)(ws + L.off_kvtab + (size_t)n * L.kvtab_bytes); };
   auto rank_of = [&](int i) { return (d->first_rank + i) % N; };
@@ -576,7 +610,12 @@ extern "C" int ringattn_run(const ra_run_desc* d, const void* const* q, const vo
                                      p->dtype, delta[i], cs)) != hipSuccess)
         return hip_fail(e, "backward preprocess kernel launch");
   if (allgather) {
-    // every block is resident: one launch per emulated rank over all of them, in ring order
+    // every block is resident: one launch per emulated rank over all of them, in ring order.
+    // The transposed value blocks are what an all-gather of V^T would deliver (each rank
+    // transposes its own block once); emulated here for all N blocks.
+    auto vth = [&](int n) { return (void*)(ws + L.off_vth + (size_t)n * L.vslot_bytes); };
+    for (int n = 0; n < N && L.vt; ++n)
+      if ((e = transpose_v(p, v_home[n], vth(n), cs)) != hipSuccess) return hip_fail(e, "value transpose kernel launch");
     if (d->step_events && d->step_events[0] && (e = hipEventRecord((hipEvent_t)d->step_events[0], cs)) != hipSuccess)
       return hip_fail(e, "hipEventRecord (step_events)");
     for (int i = 0; i < R; ++i) {
@@ -589,6 +628,7 @@ extern "C" int ringattn_run(const ra_run_desc* d, const void* const* q, const vo
         const int n = block_of(i, t);
         a.kb[t] = k_home[n];
         a.vb[t] = v_home[n];
+        if (L.vt) a.vtb[t] = vth(n);
         a.kposb[t] = kv_pos[n];
         a.kdocb[t] = doc ? kv_doc[n] : nullptr;
         a.ktilesb[t] = kvtab(n);
@@ -600,7 +640,9 @@ extern "C" int ringattn_run(const ra_run_desc* d, const void* const* q, const vo
     return ok();
   }
 
-  // Copy block (rank - t) of every emulated rank into slot t & 1.
+  // Copy block (rank - t) of every emulated rank into slot t & 1.  In the bf16 forward
+  // the value block travels transposed: its copy is the transpose kernel (always on
+  // the compute units) and step 0 transposes the home block on the compute stream.
   auto issue_copy = [&](int t) -> hipError_t {
     hipError_t err = hipSuccess;
     const int slot = t & 1;
@@ -608,13 +650,22 @@ extern "C" int ringattn_run(const ra_run_desc* d, const void* const* q, const vo
       const int n = block_of(i, t);
       if (poison) {
         if ((err = launch_fill_nan(slot_k(slot, i), copy_bytes, xs)) != hipSuccess) return err;
-        if ((err = launch_fill_nan(slot_v(slot, i), copy_bytes, xs)) != hipSuccess) return err;
+        if ((err = launch_fill_nan(slot_v(slot, i), L.vt ? vt_block_bytes(p->batch, p->hkv, p->head_dim, p->sk)
+                                                           : copy_bytes, xs)) != hipSuccess) return err;
       }
       if ((err = hipMemcpyAsync(slot_k(slot, i), k_home[n], copy_bytes, copy_kind, xs)) != hipSuccess) return err;
-      if ((err = hipMemcpyAsync(slot_v(slot, i), v_home[n], copy_bytes, copy_kind, xs)) != hipSuccess) return err;
+      if (L.vt)
+        err = transpose_v(p, v_home[n], slot_v(slot, i), xs);
+      else
+        err = hipMemcpyAsync(slot_v(slot, i), v_home[n], copy_bytes, copy_kind, xs);
+      if (err != hipSuccess) return err;
     }
     return err;
   };
+  if (L.vt && start == 0)
+    for (int i = 0; i < R; ++i)
+      if ((e = transpose_v(p, v_home[block_of(i, 0)], slot_v(0, i), cs)) != hipSuccess)
+        return hip_fail(e, "value transpose kernel launch");
 
   // Step `start` needs its block before the loop when it is not the home block.
   if (start >= 1) {
@@ -647,12 +698,13 @@ extern "C" int ringattn_run(const ra_run_desc* d, const void* const* q, const vo
     for (int i = 0; i < R; ++i) {
       const int n = block_of(i, t);
       const void* kb = t == 0 ? k_home[n] : slot_k(t & 1, i);
-      const void* vb = t == 0 ? v_home[n] : slot_v(t & 1, i);
+      const void* vb = t == 0 && !L.vt ? v_home[n] : slot_v(t & 1, i);
       if (fwd) {
         const bool merge_k = (d->flags & RA_RUN_MERGE_KERNEL) != 0 && !(flags & RA_STEP_FIRST);
         if (!merge_k) {
           FwdArgs a = make_fwd(p, q[i], kb, vb, o_acc[i], lse[i], out ? out[i] : nullptr, q_pos[i], kv_pos[n],
                                doc ? q_doc[i] : nullptr, doc ? kv_doc[n] : nullptr, qtab(i), kvtab(n), mask, flags);
+          if (L.vt) a.vb[0] = nullptr;   // only the transposed copy is staged
           if ((e = enqueue_fwd(p, a, cs)) != hipSuccess) return hip_fail(e, "forward step kernel launch");
         } else {
           float* po = (float*)(ws + L.off_part + (size_t)i * (L.part_o_bytes + L.part_l_bytes));
@@ -660,6 +712,7 @@ extern "C" int ringattn_run(const ra_run_desc* d, const void* const* q, const vo
           FwdArgs a = make_fwd(p, q[i], kb, vb, po, pl, nullptr, q_pos[i], kv_pos[n], doc ? q_doc[i] : nullptr,
                                doc ? kv_doc[n] : nullptr, qtab(i), kvtab(n), mask,
                                (flags & RA_NO_SKIP) | RA_STEP_FIRST);
+          if (L.vt) a.vb[0] = nullptr;
           if ((e = enqueue_fwd(p, a, cs)) != hipSuccess) return hip_fail(e, "forward step kernel launch");
           void* fin = (flags & RA_STEP_LAST) && out ? out[i] : nullptr;
           if ((e = launch_merge(p->batch * p->hq * p->sq, p->head_dim, po, pl, o_acc[i], lse[i], fin,

@@ -158,6 +158,16 @@ __global__ __launch_bounds__(NWAVES * 64, 1) void fwd_bf16_kernel(FwdArgs a) {
   int voff[C::CPW];
 #pragma unroll
   for (int c = 0; c < C::CPW; ++c) voff[c] = chunk_voff<D>(c * NWAVES + wave, lane, rsb);
+  // The same for the transposed value tiles (D rows of 64 keys, 128 bytes): unit p
+  // holds row p/8 (a head dimension), key unit (p%8) ^ vswz(row).
+  const int skp = a.skp;
+  const size_t vtoff = ((size_t)b * a.hkv + kvh) * D * skp;   // this (batch, kv head) within a V^T block
+  int vtoff_lane[C::CPW];
+#pragma unroll
+  for (int c = 0; c < C::CPW; ++c) {
+    const int p = (c * NWAVES + wave) * 64 + lane, r = p >> 3;
+    vtoff_lane[c] = r * skp * 2 + (((p & 7) ^ vswz(r)) << 4);
+  }
 
   // Start streaming the K rows (with the key positions and documents, wave 0)
   // / the V rows of the tile of list position li (entry ent: tile | block << 12)
@@ -176,14 +186,14 @@ __global__ __launch_bounds__(NWAVES * 64, 1) void fwd_bf16_kernel(FwdArgs a) {
     for (int c = 0; c < C::CPW; ++c)
       dma16(kb, rows * rsb, (RA_LDS void*)&Ks[buf][(c * NWAVES + wave) * 512], voff[c]);
   };
+  // V^T rows of the tile: D rows of 64 keys (the padding past the block end is zero)
   auto issue_v = [&] __device__(int li, int ent) {
     const int buf = li % NBUF, tile = ent & 0xfff, blk = (ent >> 12) & 0xf;
     const int kbase = tile * BN;
-    const int rows = min(BN, a.sk - kbase);
-    const __bf16* vb = (const __bf16*)a.vb[blk] + kvoff + (size_t)kbase * a.kvs.s;
+    const __bf16* vb = (const __bf16*)a.vtb[blk] + vtoff + kbase;
 #pragma unroll
     for (int c = 0; c < C::CPW; ++c)
-      dma16(vb, rows * rsb, (RA_LDS void*)&Vs[buf][(c * NWAVES + wave) * 512], voff[c]);
+      dma16(vb, (D * skp - kbase) * 2, (RA_LDS void*)&Vs[buf][(c * NWAVES + wave) * 512], vtoff_lane[c]);
   };
 
   // S^T = K Q^T (raw scores) of the tile in K buffer `buf`.
@@ -267,18 +277,23 @@ __global__ __launch_bounds__(NWAVES * 64, 1) void fwd_bf16_kernel(FwdArgs a) {
     l_run += rs;
   };
 
-  // O^T += V^T P^T, V^T from the row-major tile in V buffer `buf` by transpose reads.
+  // O^T += V^T P^T: V^T (lane j: head dimension db*32 + j, 8 keys) read from the
+  // transposed tile in V buffer `buf`; P^T straight from registers.
   auto pv = [&] __device__(int buf, const bf16x8(&pf)[4]) {
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk)
 #pragma unroll
-      for (int db = 0; db < D / 32; ++db) acc[db] = mfma(tr_operand<D>(Vs[buf], kk * 16, db * 32, lane), pf[kk], acc[db]);
-    constexpr int N = D / 8, AHEAD = RA_FWD_AHEAD;   // as in scores(); two transpose reads per operand
-    __builtin_amdgcn_sched_group_barrier(0x100, 2 * AHEAD, 0);
+      for (int db = 0; db < D / 32; ++db) {
+        const int r = db * 32 + j;
+        const bf16x8 vf = *(const bf16x8*)(&Vs[buf][r * BN + (((kk * 2 + g) ^ vswz(r)) << 3)]);
+        acc[db] = mfma(vf, pf[kk], acc[db]);
+      }
+    constexpr int N = D / 8, AHEAD = RA_FWD_AHEAD;   // as in scores()
+    __builtin_amdgcn_sched_group_barrier(0x100, AHEAD, 0);
 #pragma unroll
     for (int n = 0; n < N; ++n) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      if (n + AHEAD < N) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      if (n + AHEAD < N) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
   };
 

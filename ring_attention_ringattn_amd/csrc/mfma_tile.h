@@ -42,6 +42,12 @@ __device__ __forceinline__ int swz(int r) {
   return D == 128 ? 4 * (r & 3) + ((r >> 2) & 3) : 4 * ((r >> 1) & 1) + ((r >> 2) & 3);
 }
 
+// Transposed value tiles (rows of 64 keys = 8 units of 16 bytes): unit u of row r
+// is stored at u ^ vswz(r).  An operand read has 16 lanes read one unit of 16
+// consecutive rows; (row parity, u ^ vswz(r)) then takes 16 distinct values, so the
+// 16 reads hit 16 distinct 16-byte bank groups of a 256-byte window.
+__device__ __forceinline__ int vswz(int r) { return (r >> 1) & 7; }
+
 // Element offset of (row, col) in a swizzled tile; col is a multiple of 4.
 template <int D>
 __device__ __forceinline__ int tile_off(int row, int col) {

@@ -22,6 +22,10 @@ struct TileRange {
 };
 
 __host__ __device__ inline int n_tiles(int s) { return (s + TILE - 1) / TILE; }
+// keys of a transposed value block row: whole tiles
+__host__ __device__ inline int vt_keys(int sk) { return n_tiles(sk) * TILE; }
+// bytes of one transposed bf16 value block
+inline size_t vt_block_bytes(int B, int hkv, int d, int sk) { return (size_t)B * hkv * d * vt_keys(sk) * 2; }
 
 struct Strides {
   int64_t b, h, s;
@@ -54,6 +58,9 @@ struct FwdArgs {
   int n_blocks;
   const void* kb[MAX_FUSED_BLOCKS];
   const void* vb[MAX_FUSED_BLOCKS];
+  // bf16 forward: each block's values transposed, [B][Hkv][D][skp] dense (vt_transpose)
+  const void* vtb[MAX_FUSED_BLOCKS];
+  int skp;
   const int* kposb[MAX_FUSED_BLOCKS];
   const int* kdocb[MAX_FUSED_BLOCKS];
   const TileRange* ktilesb[MAX_FUSED_BLOCKS];
@@ -111,6 +118,8 @@ hipError_t launch_merge(int rows, int d, const float* o_a, const float* lse_a, f
 hipError_t launch_bwd_preprocess(int B, int hq, int sq, int d, const void* out, const void* d_o,
                                  Strides qs, int dtype, float* delta, hipStream_t st);
 hipError_t launch_fill_nan(void* p, size_t bytes, hipStream_t st);
+// V [B][Hkv][Sk][D] (strides s) -> VT [B][Hkv][D][vt_keys(Sk)] dense, zero padding
+hipError_t launch_vt_transpose(const void* v, Strides s, int B, int hkv, int sk, int d, void* vt, hipStream_t st);
 hipError_t launch_fwd_bf16(const FwdArgs& a, int d, hipStream_t st);
 hipError_t launch_fwd_f32(const FwdArgs& a, int d, hipStream_t st);
 hipError_t launch_bwd_bf16(const BwdArgs& a, int d, hipStream_t st);

@@ -143,7 +143,12 @@ def test_fused_workspace_size():
     p = _problem(sq=1000, sk=130)
     one = lib.ringattn_fused_workspace_size(ctypes.byref(p), 1)
     four = lib.ringattn_fused_workspace_size(ctypes.byref(p), 4)
-    assert one >= (16 + 3) * 16 and four - one == 3 * 256      # 3 more tile tables of 3 tiles (256-aligned)
+    # per block: a tile table of 3 tiles (256-aligned) and the bf16 transposed values,
+    # 1 batch x 2 kv heads x 128 dims x 192 keys (130 rounded up to whole 64-key tiles)
+    assert one >= (16 + 3) * 16 and four - one == 3 * (256 + 1 * 2 * 128 * 192 * 2)
+    p32 = _problem(sq=1000, sk=130, dtype=_lib.RA_F32)
+    assert lib.ringattn_fused_workspace_size(ctypes.byref(p32), 4) - \
+        lib.ringattn_fused_workspace_size(ctypes.byref(p32), 1) == 3 * 256
     assert lib.ringattn_fused_workspace_size(ctypes.byref(p), 0) == 0
     assert lib.ringattn_fused_workspace_size(ctypes.byref(p), _lib.RA_FUSED_MAX_BLOCKS + 1) == 0
 
@@ -159,6 +164,7 @@ def test_workspace_size_queries():
     p = _problem(sq=1000, sk=130)
     n = lib.ringattn_step_workspace_size(ctypes.byref(p))
     assert n >= (16 + 3) * 16 and n % 256 == 0
+    assert n >= 1 * 2 * 128 * 192 * 2     # room for the transposed value block of the bf16 forward
     assert lib.ringattn_step_workspace_size(ctypes.byref(_problem(head_dim=96))) == 0
     d = _lib.RaRunDesc()
     d.prob = _problem(sk=1024)
