@@ -94,7 +94,8 @@ __device__ __forceinline__ void map_block(int n_qt, int hq, int hkv, int total, 
 
 }  // namespace
 
-template <int D>
+// MULTI: several resident blocks (entries carry a block index); otherwise block 0 only.
+template <int D, bool MULTI>
 __global__ __launch_bounds__(NWAVES * 64, 1) void fwd_bf16_kernel(FwdArgs a) {
   using C = Cfg<D>;
   __shared__ __attribute__((aligned(1024))) __bf16 Ks[NBUF][BN * D];
@@ -169,28 +170,54 @@ __global__ __launch_bounds__(NWAVES * 64, 1) void fwd_bf16_kernel(FwdArgs a) {
     vtoff_lane[c] = r * skp * 2 + (((p & 7) ^ vswz(r)) << 4);
   }
 
+  // Block pointers of the tiles being issued.  One block: loop invariant.  Several:
+  // the list runs through the blocks in order, so each side (K, V) keeps the
+  // pointers of its current block and reloads them only when the block changes
+  // (a reload is a scalar memory load the issue must wait for).
+  const __bf16* kblk_p = (const __bf16*)a.kb[0];
+  const int* kpos_p = a.kposb[0];
+  const int* kdoc_p = a.kdocb[0];
+  const __bf16* vblk_p = (const __bf16*)a.vtb[0];
+  int kblk = 0, vblk = 0;
+
   // Start streaming the K rows (with the key positions and documents, wave 0)
   // / the V rows of the tile of list position li (entry ent: tile | block << 12)
   // into buffer li % NBUF.  Every wave issues its share; keys past the end of
   // the block read as zero.
   auto issue_k = [&] __device__(int li, int ent) {
-    const int buf = li % NBUF, tile = ent & 0xfff, blk = (ent >> 12) & 0xf;
+    const int buf = li % NBUF, tile = ent & 0xfff;
+    if (MULTI) {
+      const int blk = (ent >> 12) & 0xf;
+      if (blk != kblk) {
+        kblk = blk;
+        kblk_p = (const __bf16*)a.kb[blk];
+        kpos_p = a.kposb[blk];
+        kdoc_p = a.kdocb[blk];
+      }
+    }
     const int kbase = tile * BN;
     const int rows = min(BN, a.sk - kbase);
     if (wave == 0) {
-      dma4(a.kposb[blk] + kbase, rows * 4, (RA_LDS void*)&kvp[buf][0], lane * 4);
-      if (mask == MASK_DOC_CAUSAL) dma4(a.kdocb[blk] + kbase, rows * 4, (RA_LDS void*)&kvd[buf][0], lane * 4);
+      dma4(kpos_p + kbase, rows * 4, (RA_LDS void*)&kvp[buf][0], lane * 4);
+      if (mask == MASK_DOC_CAUSAL) dma4(kdoc_p + kbase, rows * 4, (RA_LDS void*)&kvd[buf][0], lane * 4);
     }
-    const __bf16* kb = (const __bf16*)a.kb[blk] + kvoff + (size_t)kbase * a.kvs.s;
+    const __bf16* kb = kblk_p + kvoff + (size_t)kbase * a.kvs.s;
 #pragma unroll
     for (int c = 0; c < C::CPW; ++c)
       dma16(kb, rows * rsb, (RA_LDS void*)&Ks[buf][(c * NWAVES + wave) * 512], voff[c]);
   };
   // V^T rows of the tile: D rows of 64 keys (the padding past the block end is zero)
   auto issue_v = [&] __device__(int li, int ent) {
-    const int buf = li % NBUF, tile = ent & 0xfff, blk = (ent >> 12) & 0xf;
+    const int buf = li % NBUF, tile = ent & 0xfff;
+    if (MULTI) {
+      const int blk = (ent >> 12) & 0xf;
+      if (blk != vblk) {
+        vblk = blk;
+        vblk_p = (const __bf16*)a.vtb[blk];
+      }
+    }
     const int kbase = tile * BN;
-    const __bf16* vb = (const __bf16*)a.vtb[blk] + vtoff + kbase;
+    const __bf16* vb = vblk_p + vtoff + kbase;
 #pragma unroll
     for (int c = 0; c < C::CPW; ++c)
       dma16(vb, (D * skp - kbase) * 2, (RA_LDS void*)&Vs[buf][(c * NWAVES + wave) * 512], vtoff_lane[c]);
@@ -339,16 +366,24 @@ __global__ __launch_bounds__(NWAVES * 64, 1) void fwd_bf16_kernel(FwdArgs a) {
     // Both groups run the same sequence, the trailing one shifted by one
     // barrier, so that while one group is in its matrix phase the other is in
     // its softmax phase.  Period i reads K(i) and V(i-1); in its softmax phase
-    // each group first waits for its own earlier loads (issued a period, i.e.
-    // two barriers, before) and then issues its share of K(i+3) and V(i+2),
-    // which period i+3 reads: the next wait, and two barriers, come first.
+    // each group issues its share of K(i+3) and V(i+2), which period i+3 reads.
+    // A wave waits for them at the end of the matrix phase of period i+2, just
+    // before that period's first barrier: for the leading group that barrier
+    // precedes everyone's period i+3; for the trailing group it is the barrier
+    // the leading group's period i+3 starts from.  So every load has about two
+    // periods to land, and the wait sits in the matrix phase, which is shorter
+    // than the softmax phase.
     if (!leading) __syncthreads();
     for (int i = 0; i <= total; ++i) {
       pv((i + NBUF - 1) % NBUF, pf);
       scores(i % NBUF, s);
+      // This wave's loads of period i-2 have landed (those of period i-1 may still
+      // be in flight): vmcnt = what period i-1 issued, 2 CPW for K and V, CPW for V
+      // alone (wave 0's position loads only make the wait stricter).
+      if (i + 2 < total) wait_vmem_n<2 * C::CPW>();
+      else if (i + 1 < total) wait_vmem_n<C::CPW>();
+      else wait_vmem();
       __syncthreads();
-      wait_vmem();
-      // list entries used in this phase: one LDS round trip for all three
       const int e0 = list[min(i, LIST - 1)], e2 = list[min(i + 2, LIST - 1)], e3 = list[min(i + 3, LIST - 1)];
       // list entries are workgroup-uniform: keep them scalar so the branches on them stay branches
       if (i + 3 < total) issue_k(i + 3, __builtin_amdgcn_readfirstlane(e3) & 0xffff);
@@ -397,8 +432,11 @@ __global__ __launch_bounds__(NWAVES * 64, 1) void fwd_bf16_kernel(FwdArgs a) {
 hipError_t launch_fwd_bf16(const FwdArgs& a, int d, hipStream_t st) {
   const long blocks = (long)((a.sq + BM - 1) / BM) * a.hq * a.B;
   if (blocks == 0) return hipSuccess;
-  if (d == 128) fwd_bf16_kernel<128><<<(unsigned)blocks, NWAVES * 64, 0, st>>>(a);
-  else fwd_bf16_kernel<64><<<(unsigned)blocks, NWAVES * 64, 0, st>>>(a);
+  const bool multi = a.n_blocks > 1;
+  if (d == 128 && multi) fwd_bf16_kernel<128, true><<<(unsigned)blocks, NWAVES * 64, 0, st>>>(a);
+  else if (d == 128) fwd_bf16_kernel<128, false><<<(unsigned)blocks, NWAVES * 64, 0, st>>>(a);
+  else if (multi) fwd_bf16_kernel<64, true><<<(unsigned)blocks, NWAVES * 64, 0, st>>>(a);
+  else fwd_bf16_kernel<64, false><<<(unsigned)blocks, NWAVES * 64, 0, st>>>(a);
   return hipGetLastError();
 }
 
