@@ -130,9 +130,13 @@ def setup_share(wname, ranks, with_bwd):
         docs = np.searchsorted(cu_np, np.arange(w.seq), side="right") - 1
     s["pairs_per_step"] = [sum(visible_pairs(pos[r], pos[ra.sharding.block_of(r, t, n)], docs) for r in ranks)
                            for t in range(n)]
-    s["ws"] = torch.empty(ra.ringattn_run_workspace_size(s["q"][0], s["k"][0], n, len(ranks),
-                                                         pass_=ra.RA_PASS_BWD if with_bwd else ra.RA_PASS_FWD),
-                          dtype=torch.uint8, device="cuda")
+    # one workspace for every run mode the legs use: forward ring, all-gather forward, backward ring
+    need = [ra.ringattn_run_workspace_size(s["q"][0], s["k"][0], n, len(ranks), pass_=ra.RA_PASS_FWD),
+            ra.ringattn_run_workspace_size(s["q"][0], s["k"][0], n, len(ranks), pass_=ra.RA_PASS_FWD,
+                                           flags=ra.RA_RUN_ALLGATHER)]
+    if with_bwd:
+        need.append(ra.ringattn_run_workspace_size(s["q"][0], s["k"][0], n, len(ranks), pass_=ra.RA_PASS_BWD))
+    s["ws"] = torch.empty(max(need), dtype=torch.uint8, device="cuda")
     if with_bwd:
         kshp = s["k"][0].shape
         s["delta"] = [torch.empty(shp[:3], dtype=torch.float32, device="cuda") for _ in ranks]
@@ -231,7 +235,9 @@ def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=9, help="timed rings (the pages' method: 10 runs, first dropped)")
-    ap.add_argument("--warmup", type=int, default=1)
+    ap.add_argument("--warmup", type=int, default=6,
+                    help="untimed rings first: under sustained load the shader clock settles "
+                         "(about 1.5 -> 1.84 GHz on MI355X) within the first ~50 ms")
     ap.add_argument("--rank", type=int, default=0)
     ap.add_argument("--no-bwd", action="store_true", help="skip the forward+backward legs")
     ap.add_argument("--no-cpu-baseline", action="store_true")

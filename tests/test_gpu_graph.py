@@ -31,8 +31,9 @@ def _share():
     s["dq"] = [torch.empty(x.shape, device="cuda") for x in s["q"]]
     s["dk"] = [torch.empty(x.shape, device="cuda") for x in s["k"]]
     s["dv"] = [torch.empty(x.shape, device="cuda") for x in s["k"]]
-    s["ws"] = torch.empty(ra.ringattn_run_workspace_size(s["q"][0], s["k"][0], 4, 4, pass_=ra.RA_PASS_BWD),
-                          dtype=torch.uint8, device="cuda")
+    need = max(ra.ringattn_run_workspace_size(s["q"][0], s["k"][0], 4, 4, pass_=p, flags=f)
+               for p, f in ((ra.RA_PASS_FWD, 0), (ra.RA_PASS_FWD, ra.RA_RUN_ALLGATHER), (ra.RA_PASS_BWD, 0)))
+    s["ws"] = torch.empty(need, dtype=torch.uint8, device="cuda")
     return s
 
 
