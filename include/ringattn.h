@@ -120,7 +120,9 @@ typedef struct {
 } ra_problem;
 
 /* Bytes of device workspace the step entry points need for this problem
- * (per-tile position/document ranges used to skip fully masked tiles). */
+ * (per-tile position/document ranges used to skip fully masked tiles; for
+ * bf16, room for the value block transposed to [B][Hkv][D][Sk rounded up to
+ * 64], which the forward step writes there and reads its V^T tiles from). */
 size_t ringattn_step_workspace_size(const ra_problem* p);
 
 /*
@@ -146,7 +148,8 @@ int ringattn_step_fwd(const ra_problem* p, const void* q, const void* k_blk, con
 #define RA_FUSED_MAX_BLOCKS 16
 
 /* Bytes of device workspace ringattn_fused_fwd needs (per-tile ranges of the
- * queries and of each of the n_blocks blocks). */
+ * queries and of each of the n_blocks blocks, and each value block
+ * transposed, as for ringattn_step_fwd). */
 size_t ringattn_fused_workspace_size(const ra_problem* p, int n_blocks);
 
 /*
@@ -229,7 +232,9 @@ typedef struct {
 } ra_run_desc;
 
 /* Bytes of device workspace ringattn_run needs: two staging slots of one
- * key/value block per emulated rank, plus tile tables. */
+ * key/value block per emulated rank (in the bf16 forward the value slot
+ * holds the block transposed, see ringattn_step_fwd), plus tile tables; with
+ * RA_RUN_ALLGATHER, the N value blocks transposed instead of the slots. */
 size_t ringattn_run_workspace_size(const ra_run_desc* d);
 
 /*
@@ -240,7 +245,9 @@ size_t ringattn_run_workspace_size(const ra_run_desc* d);
  * block is copied device-to-device from its home buffer into a staging slot
  * of the workspace, one step ahead, on copy_stream, double-buffered and
  * ordered with events so a slot is not overwritten before the step that
- * reads it has finished.  All arrays below are host arrays of device
+ * reads it has finished.  In the bf16 forward the value block travels
+ * transposed: its staging copy is a transpose on copy_stream, and step 0
+ * transposes the home block on compute_stream.  All arrays below are host arrays of device
  * pointers, indexed by emulated rank i (length R) or by block owner n
  * (length N).
  *
