@@ -167,11 +167,13 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
 
   const int n_items = grp * n_qt;
   const bool no_skip = (a.flags & FLAG_NO_SKIP) != 0;
+  int seen = 0;   // query tiles this workgroup processed (uniform)
   for (int c0 = 0; c0 < n_items; c0 += LIST) {
     const int total = build_list(c0, n_items, [&] __device__(int it) {
       int c = classify(a.q_tiles[it % n_qt], kr, kcomplete, mask);
       return (no_skip && c == TILE_EMPTY) ? (int)TILE_PARTIAL : c;
     }, list, wave_cnt);
+    seen += total;
     if (total == 0) continue;
     issue_tile(__builtin_amdgcn_readfirstlane(list[0]) & 0xffffff, 0);
     finish_tile(0);
@@ -236,6 +238,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
     }
   }
 
+  if (seen == 0) return;   // nothing visible: dk, dv stay as they are
   // dk, dv += ; C layout: lane (g, j), value v -> key wave*32 + 8*(v/4) + 4*g + v%4, dim db*32 + j
   const size_t obase = ((size_t)b * a.hkv + kvh) * a.sk;
 #pragma unroll
@@ -341,11 +344,13 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
 
   const int nkt = n_tiles(a.sk);
   const bool no_skip = (a.flags & FLAG_NO_SKIP) != 0;
+  int seen = 0;   // key tiles this workgroup processed (uniform)
   for (int c0 = 0; c0 < nkt; c0 += LIST) {
     const int total = build_list(c0, nkt, [&] __device__(int t) {
       int c = classify(qr, a.kv_tiles[t], (t + 1) * TILE <= a.sk, mask);
       return (no_skip && c == TILE_EMPTY) ? (int)TILE_PARTIAL : c;
     }, list, wave_cnt);
+    seen += total;
     if (total == 0) continue;
     issue_tile(__builtin_amdgcn_readfirstlane(list[0]) & 0xffffff, 0);
     finish_tile(0);
@@ -409,7 +414,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
     }
   }
 
-  if (!qvalid) return;
+  if (!qvalid || seen == 0) return;   // seen == 0: nothing visible, dq stays as it is
   // dq += scale dQ; C layout of dQ^T: lane (g, j), value v -> dim db*32 + 8*(v/4) + 4*g + v%4, query j
   float* dqp = a.dq + lrow * D;
 #pragma unroll

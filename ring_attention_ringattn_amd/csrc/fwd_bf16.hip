@@ -326,6 +326,7 @@ __global__ __launch_bounds__(NWAVES * 64, 1) void fwd_bf16_kernel(FwdArgs a) {
 
   f32x16 s[2];
   bf16x8 pf[4];
+  int seen = 0;   // tiles this workgroup processed (uniform)
   for (int c0 = 0; c0 < ntot; c0 += LIST) {
     // ---- compact the non-empty tiles of this chunk into `list` ----
     const int t = c0 + tid;
@@ -351,6 +352,7 @@ __global__ __launch_bounds__(NWAVES * 64, 1) void fwd_bf16_kernel(FwdArgs a) {
     if (cls != TILE_EMPTY) list[off + my] = tl | (blk << 12) | (cls << 24);
     __syncthreads();
     total = __builtin_amdgcn_readfirstlane(total);
+    seen += total;
     if (total == 0) continue;
     auto tile_of = [&] __device__(int li) { return __builtin_amdgcn_readfirstlane(list[li]) & 0xffff; };
 
@@ -397,6 +399,9 @@ __global__ __launch_bounds__(NWAVES * 64, 1) void fwd_bf16_kernel(FwdArgs a) {
   // ---- epilogue: normalise, merge into (o_acc, lse), optionally write out ----
   const bool first = (a.flags & FLAG_FIRST) != 0;
   const bool last = (a.flags & FLAG_LAST) != 0 && a.out != nullptr;
+  // No key of this block is visible to the tile: merging the empty partial (LSE -inf)
+  // leaves (o_acc, lse) exactly as they are, so a middle step skips the round trip.
+  if (seen == 0 && !first && !last) return;
   const float l_tot = pair_sum(l_run);
   if (!qvalid) return;
   const float lse_t = l_tot > 0.f ? (m_run + log2f(l_tot)) * LN2F : -INFINITY;
