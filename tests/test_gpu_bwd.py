@@ -155,3 +155,61 @@ def test_bwd_full_size_rank_share():
     assert e <= TOL
     for t in ring.dq + ring.dk + ring.dv:
         assert torch.isfinite(t).all()
+
+
+def test_c5_full_size_packed_documents():
+    """65536 packed tokens of lognormal documents (seed 5: 22 documents), document-causal mask,
+    4 contiguous shards, all ranks, 32/8 heads, forward + backward: the benchmark's packed
+    configuration, with the document ids made on the device from cu_seqlens as the benchmark does.
+
+    Exact per sampled row: O, LSE and dQ (random rows, the first and last row of every document
+    and the rows next to each shard boundary).  Exact per document: dK and dV of every key of two
+    whole documents -- the shortest one and the one that straddles the first shard boundary --
+    from the oracle given that document's query rows (no other row sees its keys).
+    """
+    w = synthetic.WORKLOADS["c5"]
+    print_case("c5: 65536 packed tokens, 22 documents, doc-causal, 4 contiguous shards, 32/8 heads, fwd + bwd")
+    inp = synthetic.make_inputs(w)
+    cu = inp["cu_seqlens"]
+    doc = oracle.docs_from_cu_seqlens(cu, w.seq)
+    n, S = w.n_shards, w.shard_len
+    pos = ra.sharding.shard_positions(w.seq, n, w.sharding)
+    ring = Ring(inp["q"], inp["k"], inp["v"], pos, "doc_causal", "bf16", range(n), doc=doc, do_glob=inp["do"])
+    tcu = dev(cu, torch.int32)
+    ring.q_doc = [ra.ringattn_docs_from_cu_seqlens(tcu, int(pos[r][0]), pos[r].size) for r in ring.ranks]
+    ring.kv_doc = [ra.ringattn_docs_from_cu_seqlens(tcu, int(p[0]), p.size) for p in pos]
+    ring.forward().backward()
+    for i in range(n):
+        assert np.array_equal(ring.q_doc[i].cpu().numpy(), doc[pos[i]])
+    out, lse, dq = (np.concatenate(ring.numpy(x), axis=2) for x in ("out", "lse", "dq"))
+    dk, dv = (np.concatenate(ring.numpy(x), axis=2) for x in ("dk", "dv"))   # contiguous: global order
+    assert np.all(np.isfinite(out)) and np.all(np.isfinite(lse))
+
+    rng = np.random.default_rng(5)
+    bounds = np.concatenate([cu[:-1], cu[1:] - 1, np.arange(1, n) * S - 1, np.arange(1, n) * S])
+    rows = np.unique(np.concatenate([rng.choice(w.seq, 24, replace=False), bounds]))
+    args = dict(row_block=128, skip_masked_columns=True)
+    kpos = np.arange(w.seq)
+    O, L = oracle.attention_forward(inp["q"][:, :, rows], inp["k"], inp["v"], rows, kpos, "doc_causal",
+                                    doc[rows], doc, **args)
+    print(f"  {rows.size} sampled rows: O max abs {max_abs(out[:, :, rows], O):.3g}, "
+          f"LSE max abs {max_abs(lse[:, :, rows], L):.3g}", flush=True)
+    assert max_abs(out[:, :, rows], O) <= 1e-2
+    assert max_abs(lse[:, :, rows], L) <= 1e-3
+    dQ, _, _ = oracle.attention_backward(inp["q"][:, :, rows], inp["k"], inp["v"], inp["do"][:, :, rows], rows, kpos,
+                                         "doc_causal", doc[rows], doc, **args)
+    e = rel_l2(dq[:, :, rows], dQ)
+    print(f"  sampled dQ rows rel L2 {e:.3g}", flush=True)
+    assert e <= TOL
+
+    lens = np.diff(cu)
+    straddle = int(doc[S])   # the document holding the first token of shard 1
+    assert doc[S - 1] == straddle, "the seed-5 stream has a document across the first shard boundary"
+    for d in sorted({int(np.argmin(lens)), straddle}):
+        r = np.arange(cu[d], cu[d + 1])
+        _, dK, dV = oracle.attention_backward(inp["q"][:, :, r], inp["k"], inp["v"], inp["do"][:, :, r], r, kpos,
+                                              "doc_causal", doc[r], doc, **args)
+        ek, ev = rel_l2(dk[:, :, r], dK[:, :, r]), rel_l2(dv[:, :, r], dV[:, :, r])
+        print(f"  document {d} ({r.size} tokens, keys {r[0]}..{r[-1]}): dK rel L2 {ek:.3g}, dV rel L2 {ev:.3g}",
+              flush=True)
+        assert ek <= TOL and ev <= TOL
