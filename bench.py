@@ -188,6 +188,46 @@ def fwd_bwd_leg(name, ranks, side, steps, warmup, label):
             "fwd_bwd_pct_peak": round(100.0 * (fl_f + fl_b) / (t_f + t_b) / 1e12 / PEAK_BF16_TFLOPS, 2)}
 
 
+def hbm_leg(steps, warmup):
+    """The HBM-bound kernels at the 131072-token share's shapes (16384 rows x 32 heads, D = 128):
+    the standalone LSE merge of two fp32 partials, (o_b, lse_b) <- (o_a, lse_a) (+) (o_b, lse_b),
+    which reads 2 (4D + 4) and writes 4D + 4 bytes per row and head (1548 B), and the backward
+    preprocess delta = rowsum(dO * O) over bf16 O and dO, 4D + 4 bytes per row and head (516 B).
+    Timed with events on the stream the kernels run on (torch's current stream)."""
+    import torch
+
+    import ring_attention_ringattn_amd as ra
+    B, H, S, D = 1, 32, 16384, 128
+    g = torch.Generator(device="cuda")
+    g.manual_seed(0)
+    o_a, o_b = (torch.randn(B, H, S, D, device="cuda", generator=g) for _ in range(2))
+    l_a, l_b = (torch.randn(B, H, S, device="cuda", generator=g) for _ in range(2))
+    out, d_o = (torch.randn(B, H, S, D, device="cuda", generator=g).to(torch.bfloat16) for _ in range(2))
+    delta = torch.empty(B, H, S, device="cuda")
+
+    def t(fn):
+        for _ in range(warmup):
+            fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps / 1e3
+
+    res = {}
+    for name, fn, per_row in (("merge", lambda: ra.ringattn_merge(o_a, l_a, o_b, l_b), 3 * (4 * D + 4)),
+                              ("bwd_preprocess", lambda: ra.ringattn_bwd_preprocess(out, d_o, delta), 4 * D + 4)):
+        sec = t(fn)
+        nbytes = B * H * S * per_row
+        res[name] = {"us": round(sec * 1e6, 2), "algorithmic_bytes": nbytes,
+                     "gbs": round(nbytes / sec / 1e9, 1), "frac_of_hbm_peak": round(nbytes / sec / 1e9 / PEAK_HBM_GBS, 3)}
+    return {"workload": "HBM-bound kernels at the 131072-token share's shapes (16384 rows x 32 heads, D = 128): "
+                        "standalone LSE merge of two fp32 partials, backward preprocess rowsum(dO * O)",
+            **res}
+
+
 def timed(fn, steps, warmup):
     import torch
     for _ in range(warmup):
@@ -317,6 +357,8 @@ def main():
                     "launch over every block, softmax state kept in registers, no ring steps",
         "fwd_ms": round(t_ag * 1e3, 3), "fwd_tflops": round(flops_ring / t_ag / 1e12, 2),
         "pct_peak": round(100.0 * flops_ring / t_ag / 1e12 / PEAK_BF16_TFLOPS, 2)}}
+
+    result["legs"]["hbm_kernels_131072_rank_share"] = hbm_leg(max(args.steps, 20), args.warmup)
 
     if not args.no_bwd:
         del s
