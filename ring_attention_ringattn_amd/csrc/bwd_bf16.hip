@@ -8,16 +8,19 @@
 // Two kernels, so that every output has one writer (deterministic, no
 // atomics):
 //
-// bwd_dkdv_kernel: a workgroup owns 128 keys of one kv head (32 per wave; the
-//   wave's K and V rows stay in registers as MFMA B operands) and streams the
-//   GQA group's query tiles (64 rows of Q, dO, LSE, delta, positions) through
-//   double-buffered swizzled LDS.  Per 32 query rows:
-//     S  = Q K^T, dP = dO V^T          (Q, dO rows from LDS as A operands,
-//                                        rows loaded in swap23 order)
+// bwd_dkdv_kernel: a workgroup of 8 waves owns 128 keys of one kv head, whose
+//   K and V rows it stages once in LDS, and streams the GQA group's query tiles
+//   (64 rows of Q, dO, LSE, delta, positions) through double-buffered swizzled
+//   LDS.  Wave w takes keys 32 (w % 4) .. +32 and rows 32 (w / 4) .. +32 of
+//   every tile, so two waves share each key group and each SIMD runs two waves.
+//   Per wave and tile:
+//     S  = Q K^T, dP = dO V^T          (Q, dO rows as A operands, loaded in
+//                                        swap23 order; K, V rows as B operands)
 //     P  = exp2(S c - LSE log2 e), dS = P (dP - delta)
 //     dV += P^T dO, dK += dS^T Q       (P, dS straight from registers as A
 //                                        operands; dO, Q by transpose reads)
-//   then dk, dv (fp32, owned by this workgroup) += the sums.
+//   then the two halves of each key group are summed through LDS and dk, dv
+//   (fp32, owned by this workgroup) += the sums.
 //
 // bwd_dq_kernel: a workgroup owns 128 query rows of one query head (32 per
 //   wave; Q and dO rows in registers as B operands) and streams 64-key K/V
@@ -33,9 +36,9 @@ namespace ra {
 
 namespace {
 
-constexpr int NWAVES = 4;
+constexpr int NWAVES = 4;              // dQ kernel
 constexpr int BQ = 64;                 // query rows per staged tile (dK/dV kernel)
-constexpr int BK = NWAVES * 32;        // keys per workgroup (dK/dV kernel)
+constexpr int BK = 128;                // keys per workgroup (dK/dV kernel)
 constexpr int BKT = 64;                // keys per staged tile (dQ kernel)
 constexpr int BMQ = NWAVES * 32;       // query rows per workgroup (dQ kernel)
 constexpr int LIST = 256;
@@ -66,19 +69,29 @@ __device__ __forceinline__ int build_list(int c0, int n, F cls_of, int* list, in
 }  // namespace
 
 // ------------------------------------------------------------------ dK / dV
+// A workgroup of 8 waves owns 128 keys of one kv head, held in LDS (K and V
+// are read as MFMA B operands from there); wave w takes keys 32 (w % 4) ..
+// +32 and, of every streamed 64-row query tile, rows 32 (w / 4) .. +32.  So
+// two waves share each key group and every SIMD runs two waves, one of which
+// can issue products while the other computes exponentials or waits for LDS.
+// The two partial dK, dV of a key group are summed through LDS at the end.
 template <int D>
-__global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
-  constexpr int CPW = BQ * D * 2 / 1024 / NWAVES;   // buffer->LDS chunks per wave per tile
-  __shared__ __attribute__((aligned(1024))) __bf16 Qs[2][BQ * D];
-  __shared__ __attribute__((aligned(1024))) __bf16 Os[2][BQ * D];    // dO
-  __shared__ __attribute__((aligned(16))) float lse2s[2][BQ];         // LSE log2(e); +inf: row sees nothing
+__global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a) {
+  constexpr int NW = 8;
+  constexpr int CPW = BQ * D * 2 / 1024 / NW;     // buffer->LDS chunks per wave per streamed operand
+  constexpr int KCPW = BK * D * 2 / 1024 / NW;    // ... of the stationary K (and V) tile
+  __shared__ __attribute__((aligned(1024))) __bf16 QO[2][2][BQ * D];   // [buffer][Q, dO]
+  __shared__ __attribute__((aligned(1024))) __bf16 KV[2][BK * D];      // [K, V] of the workgroup's keys
+  __shared__ __attribute__((aligned(16))) float lse2s[2][BQ];          // LSE log2(e); +inf: row sees nothing
   __shared__ __attribute__((aligned(16))) float dels[2][BQ];
   __shared__ __attribute__((aligned(16))) int qps[2][BQ];
   __shared__ __attribute__((aligned(16))) int qds[2][BQ];
   __shared__ int list[LIST];
-  __shared__ int wave_cnt[NWAVES];
+  __shared__ int wave_cnt[NW];
 
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, g = lane >> 5, j = lane & 31;
+  const int tid = threadIdx.x, lane = tid & 63, g = lane >> 5, j = lane & 31;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int kw = wave & 3, mb = wave >> 2;   // key group, row half of each query tile
   const int n_kt = (a.sk + BK - 1) / BK;
   int r = xcd_logical(blockIdx.x, n_kt * a.hkv * a.B);
   const int kt = r % n_kt; r /= n_kt;
@@ -96,17 +109,22 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
   }
   const bool kcomplete = k0 + BK <= a.sk;
 
-  // this wave's 32 keys: K and V rows as MFMA B operands (lane j = key)
-  const int key = k0 + wave * 32 + j;
-  const bool kvalid = key < a.sk;
-  const size_t koff = b * a.kvs.b + kvh * a.kvs.h + (size_t)key * a.kvs.s;
-  bf16x8 kf[D / 16], vf[D / 16];
+  // the workgroup's K and V rows into LDS (rows past the end of the block read as zero)
+  const int rsk = (int)(a.kvs.s * 2);
+  const int krows = min(BK, a.sk - k0);
+  {
+    const size_t kbase = b * a.kvs.b + kvh * a.kvs.h + (size_t)k0 * a.kvs.s;
 #pragma unroll
-  for (int ks = 0; ks < D / 16; ++ks) {
-    bf16x8 z = {};
-    kf[ks] = kvalid ? *(const bf16x8*)((const __bf16*)a.k + koff + ks * 16 + g * 8) : z;
-    vf[ks] = kvalid ? *(const bf16x8*)((const __bf16*)a.v + koff + ks * 16 + g * 8) : z;
+    for (int c = 0; c < KCPW; ++c) {
+      const int q = c * NW + wave;
+      const int vo = chunk_voff<D>(q, lane, rsk);
+      dma16((const __bf16*)a.k + kbase, krows * rsk, (RA_LDS void*)&KV[0][q * 512], vo);
+      dma16((const __bf16*)a.v + kbase, krows * rsk, (RA_LDS void*)&KV[1][q * 512], vo);
+    }
   }
+  // this lane's key (lane j of the wave's key group)
+  const int key = k0 + kw * 32 + j;
+  const bool kvalid = key < a.sk;
   const int kpos = kvalid ? a.kv_pos[key] : POS_INVALID;
   const int kdoc = (kvalid && mask == MASK_DOC_CAUSAL) ? a.kv_doc[key] : 0;
 
@@ -122,7 +140,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
   const float sl2 = a.scale_log2;
   int voff[CPW];
 #pragma unroll
-  for (int c = 0; c < CPW; ++c) voff[c] = chunk_voff<D>(c * NWAVES + wave, lane, rsb);
+  for (int c = 0; c < CPW; ++c) voff[c] = chunk_voff<D>(c * NW + wave, lane, rsb);
   unsigned rraw = 0;
   bool rok = false;
 
@@ -135,48 +153,66 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
     const size_t base = b * a.qs.b + h * a.qs.h + (size_t)q0 * a.qs.s;
 #pragma unroll
     for (int c = 0; c < CPW; ++c) {
-      const int q = c * NWAVES + wave;
-      dma16((const __bf16*)a.q + base, rows * rsb, (RA_LDS void*)&Qs[buf][q * 512], voff[c]);
-      dma16((const __bf16*)a.d_o + base, rows * rsb, (RA_LDS void*)&Os[buf][q * 512], voff[c]);
+      const int q = c * NW + wave;
+      dma16((const __bf16*)a.q + base, rows * rsb, (RA_LDS void*)&QO[buf][0][q * 512], voff[c]);
+      dma16((const __bf16*)a.d_o + base, rows * rsb, (RA_LDS void*)&QO[buf][1][q * 512], voff[c]);
     }
-    // per-row values (wave w: LSE, delta, position, document): one unconditional raw
-    // 4-byte load per thread (rows past the end reread the last row).  Nothing here may
-    // depend on the loaded value, else the wait for it would also wait for the tile loads
-    // above; finish_tile converts it.
-    const int row = tid & 63, part = tid >> 6;
-    rok = row < rows;
-    const int r = q0 + min(row, rows - 1);
-    const size_t lrow = ((size_t)b * a.hq + h) * a.sq + r;
-    const int* doc = mask == MASK_DOC_CAUSAL ? a.q_doc : a.q_pos;
-    const unsigned* src = part == 0 ? (const unsigned*)(a.lse + lrow)
-                        : part == 1 ? (const unsigned*)(a.delta + lrow)
-                        : part == 2 ? (const unsigned*)(a.q_pos + r) : (const unsigned*)(doc + r);
-    rraw = *src;
+    // per-row values (waves 0-3: LSE, delta, position, document): one unconditional raw
+    // 4-byte load per thread, converted by finish_tile (rows past the end reread the last row)
+    if (tid < 4 * 64) {
+      const int row = tid & 63, part = tid >> 6;
+      rok = row < rows;
+      const int rr = q0 + min(row, rows - 1);
+      const size_t lrow = ((size_t)b * a.hq + h) * a.sq + rr;
+      const int* doc = mask == MASK_DOC_CAUSAL ? a.q_doc : a.q_pos;
+      const unsigned* src = part == 0 ? (const unsigned*)(a.lse + lrow)
+                          : part == 1 ? (const unsigned*)(a.delta + lrow)
+                          : part == 2 ? (const unsigned*)(a.q_pos + rr) : (const unsigned*)(doc + rr);
+      rraw = *src;
+    }
   };
   auto finish_tile = [&] __device__(int buf) {
     wait_vmem();
-    const int row = tid & 63, part = tid >> 6;
-    const float f = __uint_as_float(rraw);
-    const int iv = (int)rraw;
-    // LSE in log2 units; +inf for rows past the end or that see no key (P = 0 there)
-    if (part == 0) lse2s[buf][row] = (rok && f != -INFINITY) ? f * LOG2E : INFINITY;
-    else if (part == 1) dels[buf][row] = rok ? f : 0.f;
-    else if (part == 2) qps[buf][row] = rok ? iv : -1;
-    else qds[buf][row] = (rok && mask == MASK_DOC_CAUSAL) ? iv : 0;
+    if (tid < 4 * 64) {
+      const int row = tid & 63, part = tid >> 6;
+      const float f = __uint_as_float(rraw);
+      const int iv = (int)rraw;
+      if (part == 0) lse2s[buf][row] = (rok && f != -INFINITY) ? f * LOG2E : INFINITY;
+      else if (part == 1) dels[buf][row] = rok ? f : 0.f;
+      else if (part == 2) qps[buf][row] = rok ? iv : -1;
+      else qds[buf][row] = (rok && mask == MASK_DOC_CAUSAL) ? iv : 0;
+    }
   };
 
   const int n_items = grp * n_qt;
   const bool no_skip = (a.flags & FLAG_NO_SKIP) != 0;
   int seen = 0;   // query tiles this workgroup processed (uniform)
   for (int c0 = 0; c0 < n_items; c0 += LIST) {
-    const int total = build_list(c0, n_items, [&] __device__(int it) {
-      int c = classify(a.q_tiles[it % n_qt], kr, kcomplete, mask);
-      return (no_skip && c == TILE_EMPTY) ? (int)TILE_PARTIAL : c;
-    }, list, wave_cnt);
+    // list of the non-empty items of this chunk (classified by the first LIST threads)
+    const int i = c0 + tid;
+    int cls = TILE_EMPTY;
+    if (tid < LIST && i < n_items) {
+      cls = classify(a.q_tiles[i % n_qt], kr, kcomplete, mask);
+      if (no_skip && cls == TILE_EMPTY) cls = TILE_PARTIAL;
+    }
+    const unsigned long long bal = __ballot(cls != TILE_EMPTY);
+    const int my = __popcll(bal & ((1ull << lane) - 1ull));
+    if (lane == 0) wave_cnt[wave] = __popcll(bal);
+    __syncthreads();
+    int off = 0, total = 0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      const int c = wave_cnt[w];
+      off += (w < wave) ? c : 0;
+      total += c;
+    }
+    if (cls != TILE_EMPTY) list[off + my] = i | (cls << 24);
+    __syncthreads();
+    total = __builtin_amdgcn_readfirstlane(total);
     seen += total;
     if (total == 0) continue;
     issue_tile(__builtin_amdgcn_readfirstlane(list[0]) & 0xffffff, 0);
-    finish_tile(0);
+    finish_tile(0);   // also waits for the stationary K, V loads of the first chunk
     __syncthreads();
 
     for (int li = 0; li < total; ++li) {
@@ -186,71 +222,85 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
       const bool more = li + 1 < total;
       if (more) issue_tile(__builtin_amdgcn_readfirstlane(list[li + 1]) & 0xffffff, buf ^ 1);
 
+      f32x16 s = {}, dp = {};
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb) {
-        f32x16 s = {}, dp = {};
+      for (int ks = 0; ks < D / 16; ++ks) {
+        const int off = tile_off<D>(mb * 32 + swap23(j), ks * 16 + g * 8);
+        const int koff = tile_off<D>(kw * 32 + j, ks * 16 + g * 8);
+        s = mfma(*(const bf16x8*)&QO[buf][0][off], *(const bf16x8*)&KV[0][koff], s);
+        dp = mfma(*(const bf16x8*)&QO[buf][1][off], *(const bf16x8*)&KV[1][koff], dp);
+      }
+      // lane (g, j), value v = hh*8 + e: query row mb*32 + 16*hh + 8*g + e, key j
+      bf16x8 pb[2], db_[2];
 #pragma unroll
-        for (int ks = 0; ks < D / 16; ++ks) {
-          const int off = tile_off<D>(mb * 32 + swap23(j), ks * 16 + g * 8);
-          s = mfma(*(const bf16x8*)&Qs[buf][off], kf[ks], s);
-          dp = mfma(*(const bf16x8*)&Os[buf][off], vf[ks], dp);
-        }
-        // lane (g, j), value v = hh*8 + e: query row mb*32 + 16*hh + 8*g + e, key j
-        bf16x8 pb[2], db_[2];
-#pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {
-          const int rbase = mb * 32 + 16 * hh + 8 * g;
-          const f32x4 l0 = *(const f32x4*)&lse2s[buf][rbase], l1 = *(const f32x4*)&lse2s[buf][rbase + 4];
-          const f32x4 d0 = *(const f32x4*)&dels[buf][rbase], d1 = *(const f32x4*)&dels[buf][rbase + 4];
-          if (partial) {
-            asm volatile("" ::: "memory");   // keep this a real branch
-            const i32x4 p0 = *(const i32x4*)&qps[buf][rbase], p1 = *(const i32x4*)&qps[buf][rbase + 4];
-            const i32x4 q0 = *(const i32x4*)&qds[buf][rbase], q1 = *(const i32x4*)&qds[buf][rbase + 4];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-              const int qp = e < 4 ? p0[e] : p1[e - 4];
-              const int qd = e < 4 ? q0[e] : q1[e - 4];
-              bool ok = true;
-              if (mask != MASK_NONE) ok = kpos <= qp;
-              if (mask == MASK_DOC_CAUSAL) ok = ok && kdoc == qd;
-              s[hh * 8 + e] = ok ? s[hh * 8 + e] : -INFINITY;
-            }
-          }
+      for (int hh = 0; hh < 2; ++hh) {
+        const int rbase = mb * 32 + 16 * hh + 8 * g;
+        const f32x4 l0 = *(const f32x4*)&lse2s[buf][rbase], l1 = *(const f32x4*)&lse2s[buf][rbase + 4];
+        const f32x4 d0 = *(const f32x4*)&dels[buf][rbase], d1 = *(const f32x4*)&dels[buf][rbase + 4];
+        if (partial) {
+          asm volatile("" ::: "memory");   // keep this a real branch
+          const i32x4 p0 = *(const i32x4*)&qps[buf][rbase], p1 = *(const i32x4*)&qps[buf][rbase + 4];
+          const i32x4 q0 = *(const i32x4*)&qds[buf][rbase], q1 = *(const i32x4*)&qds[buf][rbase + 4];
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
-            const float l2 = e < 4 ? l0[e] : l1[e - 4];
-            const float de = e < 4 ? d0[e] : d1[e - 4];
-            const float p = fast_exp2(__builtin_fmaf(s[hh * 8 + e], sl2, -l2));
-            pb[hh][e] = (__bf16)p;
-            db_[hh][e] = (__bf16)(p * (dp[hh * 8 + e] - de));
+            const int qp = e < 4 ? p0[e] : p1[e - 4];
+            const int qd = e < 4 ? q0[e] : q1[e - 4];
+            bool ok = true;
+            if (mask != MASK_NONE) ok = kpos <= qp;
+            if (mask == MASK_DOC_CAUSAL) ok = ok && kdoc == qd;
+            s[hh * 8 + e] = ok ? s[hh * 8 + e] : -INFINITY;
           }
         }
 #pragma unroll
-        for (int hh = 0; hh < 2; ++hh)
-#pragma unroll
-          for (int db = 0; db < D / 32; ++db) {
-            dv[db] = mfma(pb[hh], tr_operand<D>(Os[buf], mb * 32 + 16 * hh, db * 32, lane), dv[db]);
-            dk[db] = mfma(db_[hh], tr_operand<D>(Qs[buf], mb * 32 + 16 * hh, db * 32, lane), dk[db]);
-          }
+        for (int e = 0; e < 8; ++e) {
+          const float l2 = e < 4 ? l0[e] : l1[e - 4];
+          const float de = e < 4 ? d0[e] : d1[e - 4];
+          const float p = fast_exp2(__builtin_fmaf(s[hh * 8 + e], sl2, -l2));
+          pb[hh][e] = (__bf16)p;
+          db_[hh][e] = (__bf16)(p * (dp[hh * 8 + e] - de));
+        }
       }
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) {
+          dv[db] = mfma(pb[hh], tr_operand<D>(QO[buf][1], mb * 32 + 16 * hh, db * 32, lane), dv[db]);
+          dk[db] = mfma(db_[hh], tr_operand<D>(QO[buf][0], mb * 32 + 16 * hh, db * 32, lane), dk[db]);
+        }
       if (more) finish_tile(buf ^ 1);
       __syncthreads();
     }
   }
 
-  if (seen == 0) return;   // nothing visible: dk, dv stay as they are
-  // dk, dv += ; C layout: lane (g, j), value v -> key wave*32 + 8*(v/4) + 4*g + v%4, dim db*32 + j
+  wait_vmem();              // the stationary K, V loads, when no chunk had a visible tile
+  if (seen == 0) return;   // nothing visible: dk, dv stay as they are (uniform over the workgroup)
+  // Sum the two row halves of each key group through LDS: waves 4-7 hand their dK to
+  // waves 0-3 (which write dK), waves 0-3 hand their dV to waves 4-7 (which write dV).
+  __syncthreads();
+  float* xk = (float*)&QO[0][0][0];   // 4 key groups x D/32 x 16 values x 64 lanes floats
+  float* xv = (float*)&KV[0][0];
+  auto slot = [&] __device__(int db, int v) { return ((kw * (D / 32) + db) * 16 + v) * 64 + lane; };
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      if (mb == 1) xk[slot(db, v)] = dk[db][v];
+      else xv[slot(db, v)] = dv[db][v];
+    }
+  __syncthreads();
+  // C layout: lane (g, j), value v -> key kw*32 + 8*(v/4) + 4*g + v%4, dim db*32 + j
   const size_t obase = ((size_t)b * a.hkv + kvh) * a.sk;
+  float* dst = mb == 0 ? a.dk : a.dv;
+  const float sc = mb == 0 ? a.scale : 1.f;
 #pragma unroll
   for (int v = 0; v < 16; ++v) {
-    const int kr_ = k0 + wave * 32 + 8 * (v / 4) + 4 * g + (v % 4);
+    const int kr_ = k0 + kw * 32 + 8 * (v / 4) + 4 * g + (v % 4);
     if (kr_ >= a.sk) continue;
-    float* dkp = a.dk + (obase + kr_) * D;
-    float* dvp = a.dv + (obase + kr_) * D;
+    float* p = dst + (obase + kr_) * D;
 #pragma unroll
     for (int db = 0; db < D / 32; ++db) {
-      dkp[db * 32 + j] += a.scale * dk[db][v];
-      dvp[db * 32 + j] += dv[db][v];
+      const float tot = mb == 0 ? dk[db][v] + xk[slot(db, v)] : dv[db][v] + xv[slot(db, v)];
+      p[db * 32 + j] += sc * tot;
     }
   }
 }
@@ -435,10 +485,10 @@ hipError_t launch_bwd_bf16(const BwdArgs& a, int d, hipStream_t st) {
   if (dq_blocks == 0 || kv_blocks == 0) return hipSuccess;
   if (d == 128) {
     bwd_dq_kernel<128><<<(unsigned)dq_blocks, 256, 0, st>>>(a);
-    bwd_dkdv_kernel<128><<<(unsigned)kv_blocks, 256, 0, st>>>(a);
+    bwd_dkdv_kernel<128><<<(unsigned)kv_blocks, 512, 0, st>>>(a);
   } else {
     bwd_dq_kernel<64><<<(unsigned)dq_blocks, 256, 0, st>>>(a);
-    bwd_dkdv_kernel<64><<<(unsigned)kv_blocks, 256, 0, st>>>(a);
+    bwd_dkdv_kernel<64><<<(unsigned)kv_blocks, 512, 0, st>>>(a);
   }
   return hipGetLastError();
 }
