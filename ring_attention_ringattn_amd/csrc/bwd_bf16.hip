@@ -338,13 +338,9 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
   const int qrow = q0 + wave * 32 + j;
   const bool qvalid = qrow < a.sq;
   const size_t qoff = b * a.qs.b + h * a.qs.h + (size_t)qrow * a.qs.s;
+  // (loaded once the first tile list with a visible tile exists)
   bf16x8 qf[D / 16], of[D / 16];
-#pragma unroll
-  for (int ks = 0; ks < D / 16; ++ks) {
-    bf16x8 z = {};
-    qf[ks] = qvalid ? *(const bf16x8*)((const __bf16*)a.q + qoff + ks * 16 + g * 8) : z;
-    of[ks] = qvalid ? *(const bf16x8*)((const __bf16*)a.d_o + qoff + ks * 16 + g * 8) : z;
-  }
+  bool q_loaded = false;
   const size_t lrow = ((size_t)b * a.hq + h) * a.sq + qrow;
   float lse2 = INFINITY, delta = 0.f;
   if (qvalid) {
@@ -402,6 +398,15 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
     }, list, wave_cnt);
     seen += total;
     if (total == 0) continue;
+    if (!q_loaded) {
+#pragma unroll
+      for (int ks = 0; ks < D / 16; ++ks) {
+        bf16x8 z = {};
+        qf[ks] = qvalid ? *(const bf16x8*)((const __bf16*)a.q + qoff + ks * 16 + g * 8) : z;
+        of[ks] = qvalid ? *(const bf16x8*)((const __bf16*)a.d_o + qoff + ks * 16 + g * 8) : z;
+      }
+      q_loaded = true;
+    }
     issue_tile(__builtin_amdgcn_readfirstlane(list[0]) & 0xffffff, 0);
     finish_tile(0);
     __syncthreads();

@@ -130,12 +130,10 @@ __global__ __launch_bounds__(NWAVES * 64, 1) void fwd_bf16_kernel(FwdArgs a) {
   const __bf16* qptr = (const __bf16*)a.q + b * a.qs.b + h * a.qs.h;
   const int qrow = q0 + wave * 32 + j;
   const bool qvalid = qrow < a.sq;
+  // (loaded once the first tile list with a visible tile exists: a workgroup that
+  // sees no key of the block never reads its queries)
   bf16x8 qf[D / 16];
-#pragma unroll
-  for (int ks = 0; ks < D / 16; ++ks) {
-    bf16x8 z = {};
-    qf[ks] = qvalid ? *(const bf16x8*)(qptr + qrow * a.qs.s + ks * 16 + g * 8) : z;
-  }
+  bool q_loaded = false;
   const int qpos = qvalid ? a.q_pos[qrow] : -1;
   const int qdoc = (qvalid && mask == MASK_DOC_CAUSAL) ? a.q_doc[qrow] : 0;
 
@@ -354,6 +352,14 @@ __global__ __launch_bounds__(NWAVES * 64, 1) void fwd_bf16_kernel(FwdArgs a) {
     total = __builtin_amdgcn_readfirstlane(total);
     seen += total;
     if (total == 0) continue;
+    if (!q_loaded) {
+#pragma unroll
+      for (int ks = 0; ks < D / 16; ++ks) {
+        bf16x8 z = {};
+        qf[ks] = qvalid ? *(const bf16x8*)(qptr + qrow * a.qs.s + ks * 16 + g * 8) : z;
+      }
+      q_loaded = true;
+    }
     auto tile_of = [&] __device__(int li) { return __builtin_amdgcn_readfirstlane(list[li]) & 0xffff; };
 
     // prologue: K(0..2), V(0..1); V(-1) := 0 and P := 0 so that period 0's PV adds nothing
