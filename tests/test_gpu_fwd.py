@@ -271,6 +271,32 @@ def test_merge_entry_point():
         assert max_abs(tb.cpu().numpy(), ro) <= 1e-5
 
 
+
+def test_merge_full_size_sampled_rows():
+    """ringattn_merge at the 131072-token share's shape (16384 rows x 32 heads, D = 128), the launch
+    the benchmark times: sampled rows against the oracle's merge, every row finite."""
+    print_case("ringattn_merge, 1 x 32 x 16384 x 128 fp32 partials")
+    rng = np.random.default_rng(31)
+    shp = (1, 32, 16384, 128)
+    oa = rng.standard_normal(shp, dtype=np.float32)
+    ob = rng.standard_normal(shp, dtype=np.float32)
+    la = (rng.standard_normal(shp[:3]) * 4).astype(np.float32)
+    lb = (rng.standard_normal(shp[:3]) * 4).astype(np.float32)
+    la[0, 3, :100] = -np.inf
+    oa[0, 3, :100] = 0
+    ta, tla, tb, tlb = dev(oa), dev(la), dev(ob), dev(lb)
+    ra.ringattn_merge(ta, tla, tb, tlb)
+    torch.cuda.synchronize()
+    got_o, got_l = tb.cpu().numpy(), tlb.cpu().numpy()
+    assert np.all(np.isfinite(got_o)) and np.all(np.isfinite(got_l))
+    heads = np.arange(32)
+    rows = np.unique(np.concatenate([rng.choice(16384, 64, replace=False), [0, 1, 99, 100, 16383]]))
+    sel = np.ix_([0], heads, rows)
+    f64 = lambda x: x.astype(np.float64)
+    ro, rl = oracle.merge(f64(oa[sel]), f64(la[sel]), f64(ob[sel]), f64(lb[sel]))
+    assert max_abs(got_l[sel], rl) <= 1e-5
+    assert max_abs(got_o[sel], ro) <= 1e-5
+
 def test_thd_layout_doc_causal():
     """Packed [T, H, D] token-major storage (strided views) with a document-causal mask."""
     print_case("THD layout, doc-causal, 4 contiguous shards of a 4096-token packed stream")
