@@ -23,8 +23,10 @@
 //   (fp32, owned by this workgroup) += the sums.
 //
 // bwd_dq_kernel: a workgroup owns 128 query rows of one query head (32 per
-//   wave; Q and dO rows in registers as B operands) and streams 64-key K/V
-//   tiles like the forward kernel.  Per tile:
+//   wave; Q and dO rows in registers as B operands) -- of two query heads of
+//   one GQA group when the group size is even (8 waves: the heads see the
+//   same keys under the same mask, so each K/V tile is staged once for both)
+//   -- and streams 64-key K/V tiles like the forward kernel.  Per tile:
 //     S^T = K Q^T, dP^T = V dO^T, P^T, dS^T (as above, transposed)
 //     dQ^T += K^T dS^T                  (K^T by transpose reads, dS^T from
 //                                        registers)
@@ -43,9 +45,9 @@ constexpr int BKT = 64;                // keys per staged tile (dQ kernel)
 constexpr int BMQ = NWAVES * 32;       // query rows per workgroup (dQ kernel)
 constexpr int LIST = 256;
 
-// Compact the indices i in [c0, c0 + LIST) with cls(i) != EMPTY into `list`
-// (entries i | cls << 24); returns their number.  All threads must call it.
-template <typename F>
+// Compact the indices i in [c0, c0 + NW * 64) with cls(i) != EMPTY into `list`
+// (entries i | cls << 24); returns their number.  All NW * 64 threads must call it.
+template <int NW, typename F>
 __device__ __forceinline__ int build_list(int c0, int n, F cls_of, int* list, int* wave_cnt) {
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int i = c0 + tid;
@@ -56,7 +58,7 @@ __device__ __forceinline__ int build_list(int c0, int n, F cls_of, int* list, in
   __syncthreads();
   int off = 0, total = 0;
 #pragma unroll
-  for (int w = 0; w < NWAVES; ++w) {
+  for (int w = 0; w < NW; ++w) {
     const int c = wave_cnt[w];
     off += (w < wave) ? c : 0;
     total += c;
@@ -306,24 +308,26 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a) {
 }
 
 // ------------------------------------------------------------------ dQ
-template <int D>
-__global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
-  constexpr int CPW = BKT * D * 2 / 1024 / NWAVES;
+template <int D, int NW>
+__global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void bwd_dq_kernel(BwdArgs a) {
+  constexpr int HPW = NW / 4;   // query heads per workgroup (of one GQA group: same keys, same mask)
+  constexpr int LISTN = NW * 64;
+  constexpr int CPW = BKT * D * 2 / 1024 / NW;
   __shared__ __attribute__((aligned(1024))) __bf16 Ks[2][BKT * D];
   __shared__ __attribute__((aligned(1024))) __bf16 Vs[2][BKT * D];
   __shared__ __attribute__((aligned(16))) int kvp[2][BKT];
   __shared__ __attribute__((aligned(16))) int kvd[2][BKT];
-  __shared__ int list[LIST];
-  __shared__ int wave_cnt[NWAVES];
+  __shared__ int list[LISTN];
+  __shared__ int wave_cnt[NW];
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, g = lane >> 5, j = lane & 31;
   const int n_qt = (a.sq + BMQ - 1) / BMQ;
   const int grp = a.hq / a.hkv;
-  int r = xcd_logical(blockIdx.x, n_qt * a.hq * a.B);
-  const int hh = r % grp; r /= grp;
+  int r = xcd_logical(blockIdx.x, n_qt * (a.hq / HPW) * a.B);
+  const int hp = r % (grp / HPW); r /= grp / HPW;
   const int qt = n_qt - 1 - (r % n_qt); r /= n_qt;
   const int kvh = r % a.hkv, b = r / a.hkv;
-  const int h = kvh * grp + hh;
+  const int h = kvh * grp + hp * HPW + wave / 4;
   const int q0 = qt * BMQ;
   const int mask = a.mask;
 
@@ -335,7 +339,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
   }
 
   // this wave's 32 query rows: Q and dO as MFMA B operands (lane j = row)
-  const int qrow = q0 + wave * 32 + j;
+  const int qrow = q0 + (wave & 3) * 32 + j;
   const bool qvalid = qrow < a.sq;
   const size_t qoff = b * a.qs.b + h * a.qs.h + (size_t)qrow * a.qs.s;
   // (loaded once the first tile list with a visible tile exists)
@@ -361,7 +365,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
   const float sl2 = a.scale_log2;
   int voff[CPW];
 #pragma unroll
-  for (int c = 0; c < CPW; ++c) voff[c] = chunk_voff<D>(c * NWAVES + wave, lane, rsb);
+  for (int c = 0; c < CPW; ++c) voff[c] = chunk_voff<D>(c * NW + wave, lane, rsb);
   int preg = POS_INVALID, dreg = 0;
 
   auto issue_tile = [&] __device__(int tile, int buf) {
@@ -369,7 +373,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
     const int rows = min(BKT, a.sk - kbase);
 #pragma unroll
     for (int c = 0; c < CPW; ++c) {
-      const int q = c * NWAVES + wave;
+      const int q = c * NW + wave;
       dma16(kptr + (size_t)kbase * a.kvs.s, rows * rsb, (RA_LDS void*)&Ks[buf][q * 512], voff[c]);
       dma16(vptr + (size_t)kbase * a.kvs.s, rows * rsb, (RA_LDS void*)&Vs[buf][q * 512], voff[c]);
     }
@@ -391,8 +395,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
   const int nkt = n_tiles(a.sk);
   const bool no_skip = (a.flags & FLAG_NO_SKIP) != 0;
   int seen = 0;   // key tiles this workgroup processed (uniform)
-  for (int c0 = 0; c0 < nkt; c0 += LIST) {
-    const int total = build_list(c0, nkt, [&] __device__(int t) {
+  for (int c0 = 0; c0 < nkt; c0 += LISTN) {
+    const int total = build_list<NW>(c0, nkt, [&] __device__(int t) {
       int c = classify(qr, a.kv_tiles[t], (t + 1) * TILE <= a.sk, mask);
       return (no_skip && c == TILE_EMPTY) ? (int)TILE_PARTIAL : c;
     }, list, wave_cnt);
@@ -485,14 +489,18 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
 }
 
 hipError_t launch_bwd_bf16(const BwdArgs& a, int d, hipStream_t st) {
-  const long dq_blocks = (long)((a.sq + BMQ - 1) / BMQ) * a.hq * a.B;
+  // dQ: two query heads of a GQA group per 8-wave workgroup (their K/V tiles and mask are the same)
+  const bool pair = (a.hq / a.hkv) % 2 == 0;
+  const long dq_blocks = (long)((a.sq + BMQ - 1) / BMQ) * a.hq * a.B / (pair ? 2 : 1);
   const long kv_blocks = (long)((a.sk + BK - 1) / BK) * a.hkv * a.B;
   if (dq_blocks == 0 || kv_blocks == 0) return hipSuccess;
   if (d == 128) {
-    bwd_dq_kernel<128><<<(unsigned)dq_blocks, 256, 0, st>>>(a);
+    if (pair) bwd_dq_kernel<128, 8><<<(unsigned)dq_blocks, 512, 0, st>>>(a);
+    else bwd_dq_kernel<128, 4><<<(unsigned)dq_blocks, 256, 0, st>>>(a);
     bwd_dkdv_kernel<128><<<(unsigned)kv_blocks, 512, 0, st>>>(a);
   } else {
-    bwd_dq_kernel<64><<<(unsigned)dq_blocks, 256, 0, st>>>(a);
+    if (pair) bwd_dq_kernel<64, 8><<<(unsigned)dq_blocks, 512, 0, st>>>(a);
+    else bwd_dq_kernel<64, 4><<<(unsigned)dq_blocks, 256, 0, st>>>(a);
     bwd_dkdv_kernel<64><<<(unsigned)kv_blocks, 512, 0, st>>>(a);
   }
   return hipGetLastError();
