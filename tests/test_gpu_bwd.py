@@ -80,15 +80,17 @@ def test_bwd_doc_causal_thd_all_ranks():
     _check(ring, inp, "doc_causal", doc)
 
 
-@pytest.mark.parametrize("case", [("none", 64, 130, 200), ("causal", 64, 257, 190), ("causal", 128, 100, 333)],
+@pytest.mark.parametrize("case", [("none", 64, 130, 200), ("causal", 64, 257, 190), ("causal", 128, 100, 333),
+                                  # odd GQA group sizes (MHA, 3 heads per kv head): one query head per dQ workgroup
+                                  ("none", 64, 130, 200, 2, 2), ("causal", 128, 100, 333, 3, 1)],
                          ids=lambda c: "-".join(map(str, c)))
 def test_step_bwd_ragged(case):
     """One backward step on ragged sizes with scattered positions (step entry point, D=64 and 128)."""
-    mask, d, sq, sk = case
+    mask, d, sq, sk, *heads = case
     print_case(f"step_bwd {case}")
     rng = np.random.default_rng(sq * 1000 + sk)
     rnd = lambda *s: synthetic.bf16_round(0.5 * rng.standard_normal(s).astype(np.float32))
-    B, hq, hkv = 2, 4, 2
+    B, (hq, hkv) = 2, (heads or (4, 2))
     q, k, v, do = rnd(B, hq, sq, d), rnd(B, hkv, sk, d), rnd(B, hkv, sk, d), rnd(B, hq, sq, d)
     perm = rng.permutation(sq + sk).astype(np.int32)
     qp, kp = perm[:sq], perm[sq:]
