@@ -406,8 +406,10 @@ __global__ __launch_bounds__(NWAVES * 64, 1) void fwd_bf16_kernel(FwdArgs a) {
   const bool first = (a.flags & FLAG_FIRST) != 0;
   const bool last = (a.flags & FLAG_LAST) != 0 && a.out != nullptr;
   // No key of this block is visible to the tile: merging the empty partial (LSE -inf)
-  // leaves (o_acc, lse) exactly as they are, so a middle step skips the round trip.
-  if (seen == 0 && !first && !last) return;
+  // leaves (o_acc, lse) exactly as they are, so a middle step skips the round trip and
+  // the last step only writes the bf16 output.
+  const bool unchanged = seen == 0 && !first;
+  if (unchanged && !last) return;
   const float l_tot = pair_sum(l_run);
   if (!qvalid) return;
   const float lse_t = l_tot > 0.f ? (m_run + log2f(l_tot)) * LN2F : -INFINITY;
@@ -430,14 +432,14 @@ __global__ __launch_bounds__(NWAVES * 64, 1) void fwd_bf16_kernel(FwdArgs a) {
       f32x4 o = {acc[db][vh * 4 + 0] * w_t, acc[db][vh * 4 + 1] * w_t, acc[db][vh * 4 + 2] * w_t,
                  acc[db][vh * 4 + 3] * w_t};
       if (!first) o += w_p * *(const f32x4*)(op + d);
-      if (op) *(f32x4*)(op + d) = o;
+      if (op && !unchanged) *(f32x4*)(op + d) = o;
       if (last) {
         bf16x4 ob = {(__bf16)o[0], (__bf16)o[1], (__bf16)o[2], (__bf16)o[3]};
         *(bf16x4*)(outp + d) = ob;
       }
     }
   }
-  if (g == 0) a.lse[orow] = lse_new;
+  if (g == 0 && !unchanged) a.lse[orow] = lse_new;
 }
 
 hipError_t launch_fwd_bf16(const FwdArgs& a, int d, hipStream_t st) {
