@@ -343,6 +343,9 @@ def main():
                    "rank": args.rank, "global_batch": 1, "seq_len": w.seq, "local_queries": int(s["pos"][args.rank].size),
                    "ring_steps": n, "parallelism": "cp8 (ring emulated on one GPU)"},
         "pct_peak": round(100.0 * flops_ring / t_ring / 1e12 / PEAK_BF16_TFLOPS, 2),
+        # ring time not covered by the step kernels: launch gaps between steps, the tile tables, the
+        # transpose of step 0's home value block on the compute stream, and any wait for a staging copy
+        "exposed_ms_per_ring": round(t_ring * 1e3 - sum(kern_ms), 4),
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": measured_traffic(),
                      "kernel": "ra::fwd_bf16_kernel<128,*>",
