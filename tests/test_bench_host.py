@@ -1,0 +1,61 @@
+"""Host logic of bench.py (no GPU): the multi-GPU refusal and the FLOP accounting.
+
+The benchmark's throughput is causal-effective: FLOPs are counted from the number
+of visible (query, key) pairs, so that count is checked here against closed forms
+of zigzag sharding (every rank sees 2N c^2 + c pairs per head, c = S / 2N) and
+against the packed-document count of the seed-5 lognormal stream (each document
+of length L contributes L (L + 1) / 2 pairs).
+"""
+import os
+import subprocess
+import sys
+
+import numpy as np
+
+import bench
+import ring_attention_ringattn_amd as ra
+import synthetic
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=120)
+    assert r.returncode == 2
+    assert "--gpus 2" in r.stderr and "single MI355X" in r.stderr
+    assert r.stdout == ""
+
+
+def _pairs_per_step(name, rank):
+    w = synthetic.WORKLOADS[name]
+    pos = ra.sharding.shard_positions(w.seq, w.n_shards, w.sharding)
+    return [bench.visible_pairs(pos[rank], pos[ra.sharding.block_of(rank, t, w.n_shards)]) for t in range(w.n_shards)]
+
+
+def test_zigzag_rank_share_pair_counts():
+    for name, total in (("c3", 1_073_750_016), ("c4", 4_294_983_680)):
+        w = synthetic.WORKLOADS[name]
+        c = w.seq // (2 * w.n_shards)
+        steps = _pairs_per_step(name, 0)
+        assert sum(steps) == total == 2 * w.n_shards * c * c + c
+        # the home block (step 0) adds the diagonal c; every other step sees exactly 2 c^2
+        assert steps[0] == 2 * c * c + c and all(p == 2 * c * c for p in steps[1:])
+    # every rank of the 8192-token ring sees the same count
+    w = synthetic.WORKLOADS["c2"]
+    c = w.seq // (2 * w.n_shards)
+    assert {sum(_pairs_per_step("c2", r)) for r in range(w.n_shards)} == {2 * w.n_shards * c * c + c}
+
+
+def test_packed_document_pair_count():
+    w = synthetic.WORKLOADS["c5"]
+    cu = synthetic.cu_seqlens(w)
+    lens = np.diff(cu).astype(np.int64)
+    assert len(lens) == 22
+    assert int((lens * (lens + 1) // 2).sum()) == 271_551_562
+    docs = np.searchsorted(cu, np.arange(w.seq), side="right") - 1
+    pos = ra.sharding.shard_positions(w.seq, w.n_shards, w.sharding)
+    n = w.n_shards
+    total = sum(bench.visible_pairs(pos[r], pos[ra.sharding.block_of(r, t, n)], docs)
+                for r in range(n) for t in range(n))
+    assert total == 271_551_562
