@@ -598,12 +598,24 @@ extern "C" int ringattn_run(const ra_run_desc* d, const void* const* q, const vo
   }
 
   // tile tables: every emulated rank's queries and every block's keys
-  for (int i = 0; i < R; ++i)
-    if ((e = launch_tile_ranges(q_pos[i], doc ? q_doc[i] : nullptr, p->sq, qtab(i), cs)) != hipSuccess)
-      return hip_fail(e, "tile-range kernel launch");
-  for (int n = 0; n < N && p->sk > 0; ++n)
-    if ((e = launch_tile_ranges(kv_pos[n], doc ? kv_doc[n] : nullptr, p->sk, kvtab(n), cs)) != hipSuccess)
-      return hip_fail(e, "tile-range kernel launch");
+  {
+    // one launch per TABLE_JOBS tables
+    TableJobs jobs{};
+    auto add = [&](TableJob jb) -> hipError_t {
+      jobs.job[jobs.count++] = jb;
+      if (jobs.count < TABLE_JOBS) return hipSuccess;
+      const hipError_t err = launch_tile_ranges_batch(jobs, cs);
+      jobs.count = 0;
+      return err;
+    };
+    for (int i = 0; i < R; ++i)
+      if ((e = add(TableJob{q_pos[i], doc ? q_doc[i] : nullptr, qtab(i), p->sq})) != hipSuccess)
+        return hip_fail(e, "tile-range kernel launch");
+    for (int n = 0; n < N && p->sk > 0; ++n)
+      if ((e = add(TableJob{kv_pos[n], doc ? kv_doc[n] : nullptr, kvtab(n), p->sk})) != hipSuccess)
+        return hip_fail(e, "tile-range kernel launch");
+    if ((e = launch_tile_ranges_batch(jobs, cs)) != hipSuccess) return hip_fail(e, "tile-range kernel launch");
+  }
   if (!fwd)
     for (int i = 0; i < R; ++i)
       if ((e = launch_bwd_preprocess(p->batch, p->hq, p->sq, p->head_dim, out[i], d_o[i], strides3(p->q_stride),

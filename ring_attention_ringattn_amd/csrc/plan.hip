@@ -27,6 +27,39 @@ __global__ __launch_bounds__(256) void tile_ranges_kernel(const int* __restrict_
   if (lane == 0) out[tile] = TileRange{mn_p, mx_p, mn_d, mx_d};
 }
 
+// Several tables in one launch: blockIdx.y selects the job.
+__global__ __launch_bounds__(256) void tile_ranges_batch_kernel(TableJobs jobs) {
+  const TableJob& jb = jobs.job[blockIdx.y];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int tiles = n_tiles(jb.n);
+  const int tile = blockIdx.x * 4 + wave;
+  if (tile >= tiles) return;
+  const int t = tile * TILE + lane;
+  const bool valid = t < jb.n;
+  int p = valid ? jb.pos[t] : 0;
+  int d = (valid && jb.doc) ? jb.doc[t] : 0;
+  int mn_p = valid ? p : 0x7fffffff, mx_p = valid ? p : (int)0x80000000;
+  int mn_d = valid ? d : 0x7fffffff, mx_d = valid ? d : (int)0x80000000;
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    mn_p = min(mn_p, __shfl_xor(mn_p, off));
+    mx_p = max(mx_p, __shfl_xor(mx_p, off));
+    mn_d = min(mn_d, __shfl_xor(mn_d, off));
+    mx_d = max(mx_d, __shfl_xor(mx_d, off));
+  }
+  if (lane == 0) jb.out[tile] = TileRange{mn_p, mx_p, mn_d, mx_d};
+}
+
+hipError_t launch_tile_ranges_batch(const TableJobs& jobs, hipStream_t st) {
+  if (jobs.count <= 0) return hipSuccess;
+  if (jobs.count > TABLE_JOBS) return hipErrorInvalidValue;
+  int tiles = 0;
+  for (int i = 0; i < jobs.count; ++i) tiles = max(tiles, n_tiles(jobs.job[i].n));
+  if (tiles == 0) return hipSuccess;
+  tile_ranges_batch_kernel<<<dim3((tiles + 3) / 4, jobs.count), 256, 0, st>>>(jobs);
+  return hipGetLastError();
+}
+
 hipError_t launch_tile_ranges(const int* pos, const int* doc, int n, TileRange* out, hipStream_t st) {
   const int tiles = n_tiles(n);
   if (tiles == 0) return hipSuccess;

@@ -112,6 +112,19 @@ __host__ __device__ inline int classify(const TileRange& qr, const TileRange& kr
 
 // ---- launchers (each returns hipGetLastError() of its launches) ----
 hipError_t launch_tile_ranges(const int* pos, const int* doc, int n, TileRange* out, hipStream_t st);
+// Several tile tables in one launch (the ring builds one per emulated rank's queries and per block).
+constexpr int TABLE_JOBS = 48;
+struct TableJob {
+  const int* pos;
+  const int* doc;   // null: every token in document 0
+  TileRange* out;
+  int n;
+};
+struct TableJobs {
+  TableJob job[TABLE_JOBS];
+  int count;
+};
+hipError_t launch_tile_ranges_batch(const TableJobs& jobs, hipStream_t st);
 hipError_t launch_docs_from_cu(const int* cu, int n_docs, int first, int n, int* doc, hipStream_t st);
 hipError_t launch_merge(int rows, int d, const float* o_a, const float* lse_a, float* o_b, float* lse_b,
                         void* out, Strides os, int hq, int sq, int dtype, hipStream_t st);
