@@ -9,9 +9,10 @@
 //                         the wave's Q rows held in registers (B)
 //   mask + online softmax each lane owns whole query columns of S^T, so the
 //                         running max/sum need one cross-lane exchange
-//   O^T += V^T P^T        V^T read from the row-major V tile with the LDS
-//                         transpose read (A); P^T straight from the S^T
-//                         accumulator registers (B), converted to bf16
+//   O^T += V^T P^T        V^T (A) from the transposed value tile (the value
+//                         block is staged as V^T, so a plain 16-byte read);
+//                         P^T (B) straight from the S^T accumulator
+//                         registers, converted to bf16
 //
 // Making the S^T accumulator usable as the P^T operand without a shuffle:
 // lane l of a 32x32 MFMA result holds rows {8*(v/4) + 4*(l/32) + v%4}, but
@@ -32,12 +33,13 @@
 //                       trailing group  PV(i-1), S(i)
 //
 // so on every SIMD one wave feeds the matrix core while the other computes
-// exponentials.  Both phases of period i read the same two tiles, K(i) and
-// V(i-1); K(i+1) and V(i) stream from HBM straight into LDS (buffer loads,
-// no register staging, zero-fill past the end of the block) during period i
-// into the other halves of double buffers.  Tiles are row-major and
-// swizzled (mfma_tile.h) so the K operand reads and the V transpose reads
-// are free of bank conflicts.
+// exponentials (and reads the first key group of V(i) for the next PV: a lone
+// wave's LDS read rate is what holds the matrix phase back).  Both phases of
+// period i read the same two tiles, K(i) and V(i-1) (and V(i) for that key
+// group); later tiles stream from HBM straight into LDS (buffer loads,
+// no register staging, zero-fill past the end of the block) into 4-deep
+// buffers, K three tiles ahead and V two.  Tiles are swizzled (mfma_tile.h)
+// so the K and V^T operand reads are free of bank conflicts.
 //
 // Online softmax with a lazily updated maximum: the running maximum m only
 // moves when a tile's maximum exceeds it by more than RESCALE_SLACK (log2
@@ -221,26 +223,48 @@ __global__ __launch_bounds__(NWAVES * 64, 1) void fwd_bf16_kernel(FwdArgs a) {
       dma16(vb, (D * skp - kbase) * 2, (RA_LDS void*)&Vs[buf][(c * NWAVES + wave) * 512], vtoff_lane[c]);
   };
 
-  // S^T = K Q^T (raw scores) of the tile in K buffer `buf`.
-  auto scores = [&] __device__(int buf, f32x16(&s)[2]) {
+  // V^T operands (lane j: head dimension db*32 + j, 8 keys) of the transposed tile in V
+  // buffer `buf`.  Those of the first key group of the next PV are read in the softmax
+  // phase, where the other wave of the SIMD reads its own operands: one wave alone gets
+  // about 1 KB of LDS data per 40 cycles, less than a 32-cycle MFMA consumes.  (Reading
+  // more groups early lengthens the softmax phase by more than it saves: measured.)
+  auto v_operand = [&] __device__(int buf, int kk, int db) {
+    const int r = db * 32 + j;
+    return *(const bf16x8*)(&Vs[buf][r * BN + (((kk * 2 + g) ^ vswz(r)) << 3)]);
+  };
+  bf16x8 vpre[D / 32];
+  auto prefetch_v = [&] __device__(int buf) {
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) vpre[db] = v_operand(buf, 0, db);
+  };
+
+  // Matrix phase: O^T += V^T P^T (V buffer `vbuf`; P^T straight from registers), then
+  // S^T = K Q^T (raw scores) of the tile in K buffer `kbuf`.
+  auto matrix = [&] __device__(int vbuf, int kbuf, const bf16x8(&pf)[4], f32x16(&s)[2]) {
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) acc[db] = mfma(kk == 0 ? vpre[db] : v_operand(vbuf, kk, db), pf[kk], acc[db]);
     s[0] = f32x16{};
     s[1] = f32x16{};
 #pragma unroll
-    for (int ks = 0; ks < D / 16; ++ks) {
+    for (int ks = 0; ks < D / 16; ++ks)
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb) {
-        const bf16x8 kf = *(const bf16x8*)(&Ks[buf][tile_off<D>(mb * 32 + swap23(j), ks * 16 + g * 8)]);
+        const bf16x8 kf = *(const bf16x8*)(&Ks[kbuf][tile_off<D>(mb * 32 + swap23(j), ks * 16 + g * 8)]);
         s[mb] = mfma(kf, qf[ks], s[mb]);
       }
-    }
-    // issue order: operand reads run AHEAD products ahead of their MFMA (one wave per
-    // SIMD feeds the matrix core in this phase, so nothing else hides the LDS latency)
-    constexpr int N = D / 8, AHEAD = RA_FWD_AHEAD;
-    __builtin_amdgcn_sched_group_barrier(0x100, AHEAD, 0);
+    // issue order: each operand read runs AHEAD products ahead of its MFMA (one wave per
+    // SIMD feeds the matrix core in this phase, so nothing else hides the LDS latency);
+    // the first D/32 products take their operands from registers
+    constexpr int M = D / 4, PRE = D / 32, R = M - PRE, AH = RA_FWD_AHEAD;
 #pragma unroll
-    for (int n = 0; n < N; ++n) {
+    for (int m = 0; m < M; ++m) {
+      const int before = m + AH - PRE < 0 ? 0 : (m + AH - PRE > R ? R : m + AH - PRE);
+      const int prev = m == 0 ? 0 : (m - 1 + AH - PRE < 0 ? 0 : (m - 1 + AH - PRE > R ? R : m - 1 + AH - PRE));
+#pragma unroll
+      for (int x = 0; x < before - prev; ++x) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      if (n + AHEAD < N) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
   };
 
@@ -302,26 +326,6 @@ __global__ __launch_bounds__(NWAVES * 64, 1) void fwd_bf16_kernel(FwdArgs a) {
     l_run += rs;
   };
 
-  // O^T += V^T P^T: V^T (lane j: head dimension db*32 + j, 8 keys) read from the
-  // transposed tile in V buffer `buf`; P^T straight from registers.
-  auto pv = [&] __device__(int buf, const bf16x8(&pf)[4]) {
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk)
-#pragma unroll
-      for (int db = 0; db < D / 32; ++db) {
-        const int r = db * 32 + j;
-        const bf16x8 vf = *(const bf16x8*)(&Vs[buf][r * BN + (((kk * 2 + g) ^ vswz(r)) << 3)]);
-        acc[db] = mfma(vf, pf[kk], acc[db]);
-      }
-    constexpr int N = D / 8, AHEAD = RA_FWD_AHEAD;   // as in scores()
-    __builtin_amdgcn_sched_group_barrier(0x100, AHEAD, 0);
-#pragma unroll
-    for (int n = 0; n < N; ++n) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      if (n + AHEAD < N) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-    }
-  };
-
   f32x16 s[2];
   bf16x8 pf[4];
   int seen = 0;   // tiles this workgroup processed (uniform)
@@ -368,6 +372,8 @@ __global__ __launch_bounds__(NWAVES * 64, 1) void fwd_bf16_kernel(FwdArgs a) {
     for (int e = tid * 8; e < BN * D; e += NWAVES * 64 * 8) *(bf16x8*)&Vs[NBUF - 1][e] = bf16x8{};
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) pf[kk] = bf16x8{};
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) vpre[db] = bf16x8{};
     wait_vmem();
     __syncthreads();
 
@@ -383,8 +389,7 @@ __global__ __launch_bounds__(NWAVES * 64, 1) void fwd_bf16_kernel(FwdArgs a) {
     // than the softmax phase.
     if (!leading) __syncthreads();
     for (int i = 0; i <= total; ++i) {
-      pv((i + NBUF - 1) % NBUF, pf);
-      scores(i % NBUF, s);
+      matrix((i + NBUF - 1) % NBUF, i % NBUF, pf, s);
       // This wave's loads of period i-2 have landed (those of period i-1 may still
       // be in flight): vmcnt = what period i-1 issued, 2 CPW for K and V, CPW for V
       // alone (wave 0's position loads only make the wait stricter).
@@ -396,6 +401,7 @@ __global__ __launch_bounds__(NWAVES * 64, 1) void fwd_bf16_kernel(FwdArgs a) {
       // list entries are workgroup-uniform: keep them scalar so the branches on them stay branches
       if (i + 3 < total) issue_k(i + 3, __builtin_amdgcn_readfirstlane(e3) & 0xffff);
       if (i + 2 < total) issue_v(i + 2, __builtin_amdgcn_readfirstlane(e2) & 0xffff);
+      if (i < total) prefetch_v(i % NBUF);   // V(i), read by the next period's PV
       if (i < total) softmax(__builtin_amdgcn_readfirstlane(e0), i % NBUF, s, pf);
       __syncthreads();
     }
