@@ -153,8 +153,8 @@ int ringattn_step_fwd(const ra_problem* p, const void* q, const void* k_blk, con
 size_t ringattn_fused_workspace_size(const ra_problem* p, int n_blocks);
 
 /*
- * All-gather forward (the guide's all-gather rotation, "ring attention" page,
- * section on all-gather versus all-to-all rotation): once every K,V block is
+ * All-gather forward (the page "Context Parallel no 🤗 accelerate", section
+ * "all-to-all vs all-gather": the all-gather variant): once every K,V block is
  * resident, attention of q against all n_blocks blocks in ONE launch.  The
  * tile list of a query tile spans every block and the online-softmax state
  * stays in registers across blocks, so unlike a ring of ringattn_step_fwd

@@ -60,6 +60,33 @@ bool non_overlapping(const int64_t st[3], int64_t B, int64_t H, int64_t S, int64
   return true;
 }
 
+// A dispatch holds the work-item count of each grid dimension in 32 bits: the blocks of
+// one launch times its threads per block must fit.
+bool grid_fits(int64_t blocks, int threads) { return blocks <= (int64_t)(0xffffffffu / (unsigned)threads); }
+
+// Workgroups per row of the standalone merge (and the merge-kernel run mode): one
+// 32-lane group per (batch, head, token) row in 256-thread blocks.
+bool merge_fits(int64_t rows) { return grid_fits((rows * 32 + 255) / 256, 256); }
+
+// Every launch this problem can make (forward, backward, merge) must have a grid that
+// fits, and the per-workgroup work lists index their items in 24 bits.
+int check_launch_sizes(const ra_problem* p) {
+  const int64_t B = p->batch, hq = p->hq, hkv = p->hkv, sq = p->sq, sk = p->sk;
+  const int64_t rows = B * hq * sq, keys = B * hkv * sk;
+  bool fits = merge_fits(rows) && grid_fits((rows * (p->head_dim / 8) + 255) / 256, 256);
+  if (p->dtype == RA_BF16)
+    fits = fits && grid_fits((sq + 255) / 256 * hq * B, 512)   // forward step
+           && grid_fits((sq + 127) / 128 * hq * B, 256)        // dQ, one query head per workgroup
+           && grid_fits((sk + 127) / 128 * hkv * B, 512)       // dK/dV
+           && (hq / hkv) * ((sq + 63) / 64) < (1 << 24);       // dK/dV work items (query head, tile)
+  else
+    fits = fits && grid_fits((rows + 3) / 4, 256) && grid_fits((keys + 3) / 4, 256);
+  if (!fits)
+    return fail(RA_ERR_UNSUPPORTED, "problem too large for one launch (batch %d x hq %d x sq %d, hkv %d, sk %d)",
+                p->batch, p->hq, p->sq, p->hkv, p->sk);
+  return RA_OK;
+}
+
 int check_problem(const ra_problem* p) {
   if (!p) return fail(RA_ERR_INVALID, "problem descriptor is NULL");
   if (p->batch < 1 || p->hq < 1 || p->hkv < 1)
@@ -81,7 +108,7 @@ int check_problem(const ra_problem* p) {
     return fail(RA_ERR_INVALID, "q strides make rows overlap (out is written with them)");
   if (!std::isfinite(p->softmax_scale) || p->softmax_scale < 0.f)
     return fail(RA_ERR_INVALID, "softmax_scale must be finite and >= 0");
-  return RA_OK;
+  return check_launch_sizes(p);
 }
 
 int check_ptr(const void* ptr, const char* name, size_t align = 16) {
@@ -307,13 +334,15 @@ int ringattn_merge(const ra_problem* p, const float* o_a, const float* lse_a, fl
     return fail(RA_ERR_INVALID, "batch and hq must be >= 1 and sq >= 0");
   if (p->head_dim != 64 && p->head_dim != 128)
     return fail(RA_ERR_UNSUPPORTED, "head_dim %d not supported (64 or 128)", p->head_dim);
-  const long rows = (long)p->batch * p->hq * p->sq;
+  const int64_t rows = (int64_t)p->batch * p->hq * p->sq;
   if (rows == 0) return ok();
+  if (!merge_fits(rows))
+    return fail(RA_ERR_UNSUPPORTED, "%lld rows exceed one merge launch", (long long)rows);
   if (int rc = check_ptr(o_a, "o_a")) return rc;
   if (int rc = check_ptr(o_b, "o_b")) return rc;
   if (int rc = check_ptr(lse_a, "lse_a", 4)) return rc;
   if (int rc = check_ptr(lse_b, "lse_b", 4)) return rc;
-  hipError_t e = launch_merge((int)rows, p->head_dim, o_a, lse_a, o_b, lse_b, nullptr, Strides{0, 0, 0}, p->hq,
+  hipError_t e = launch_merge(rows, p->head_dim, o_a, lse_a, o_b, lse_b, nullptr, Strides{0, 0, 0}, p->hq,
                               p->sq, p->dtype, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "merge kernel launch");
   return ok();
@@ -727,7 +756,7 @@ extern "C" int ringattn_run(const ra_run_desc* d, const void* const* q, const vo
           if (L.vt) a.vb[0] = nullptr;
           if ((e = enqueue_fwd(p, a, cs)) != hipSuccess) return hip_fail(e, "forward step kernel launch");
           void* fin = (flags & RA_STEP_LAST) && out ? out[i] : nullptr;
-          if ((e = launch_merge(p->batch * p->hq * p->sq, p->head_dim, po, pl, o_acc[i], lse[i], fin,
+          if ((e = launch_merge((int64_t)p->batch * p->hq * p->sq, p->head_dim, po, pl, o_acc[i], lse[i], fin,
                                 strides3(p->q_stride), p->hq, p->sq, p->dtype, cs)) != hipSuccess)
             return hip_fail(e, "merge kernel launch");
         }

@@ -384,9 +384,13 @@ __global__ __launch_bounds__(NWAVES * 64, 1) void fwd_bf16_kernel(FwdArgs a) {
     // A wave waits for them at the end of the matrix phase of period i+2, just
     // before that period's first barrier: for the leading group that barrier
     // precedes everyone's period i+3; for the trailing group it is the barrier
-    // the leading group's period i+3 starts from.  So every load has about two
-    // periods to land, and the wait sits in the matrix phase, which is shorter
-    // than the softmax phase.
+    // the leading group's period i+3 starts from.  One read comes earlier: the
+    // first key group of V(i+2) is read in the softmax phase of period i+2,
+    // which for the leading group starts one barrier before the trailing
+    // group's matrix-phase wait; so the trailing group also waits at the end of
+    // its softmax phase of period i+1.  Leading loads thus have about two
+    // periods to land, trailing ones one and a half, and the waits sit where
+    // the loads are normally long done.
     if (!leading) __syncthreads();
     for (int i = 0; i <= total; ++i) {
       matrix((i + NBUF - 1) % NBUF, i % NBUF, pf, s);
@@ -403,6 +407,16 @@ __global__ __launch_bounds__(NWAVES * 64, 1) void fwd_bf16_kernel(FwdArgs a) {
       if (i + 2 < total) issue_v(i + 2, __builtin_amdgcn_readfirstlane(e2) & 0xffff);
       if (i < total) prefetch_v(i % NBUF);   // V(i), read by the next period's PV
       if (i < total) softmax(__builtin_amdgcn_readfirstlane(e0), i % NBUF, s, pf);
+      // The leading group's softmax(i+1), which starts at the next barrier, reads V(i+1)
+      // early (prefetch_v), and a quarter of that tile arrives through the trailing
+      // waves' loads of period i-1.  So the trailing group waits for those loads here,
+      // one phase earlier than its own reads need: vmcnt = what period i issued after
+      // them (K(i+3) and V(i+2), each only if it exists).
+      if (!leading && i + 1 < total) {
+        if (i + 3 < total) wait_vmem_n<2 * C::CPW>();
+        else if (i + 2 < total) wait_vmem_n<C::CPW>();
+        else wait_vmem();
+      }
       __syncthreads();
     }
     if (leading) __syncthreads();

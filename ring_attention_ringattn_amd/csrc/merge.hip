@@ -29,7 +29,7 @@ __device__ inline void combine_weights(float la, float lb, float& lse, float& wa
 // stores are nontemporal (no reuse to keep in the caches; measured: 5.1 ->
 // 6.4 TB/s on MI355X at 16384 rows x 32 heads, D = 128).
 template <int D>
-__global__ __launch_bounds__(256) void merge_kernel(int rows, const float* __restrict__ o_a,
+__global__ __launch_bounds__(256) void merge_kernel(long rows, const float* __restrict__ o_a,
                                                     const float* __restrict__ lse_a, float* o_b,
                                                     float* lse_b, void* out, Strides os, int hq, int sq,
                                                     int dtype) {
@@ -46,7 +46,7 @@ __global__ __launch_bounds__(256) void merge_kernel(int rows, const float* __res
   const vec r = wa * a + wb * b;
   __builtin_nontemporal_store(r, (vec*)(o_b + base));
   if (out) {
-    const int bi = row / (hq * sq), h = (row / sq) % hq, s = row % sq;
+    const int bi = row / ((long)hq * sq), h = (row / sq) % hq, s = row % sq;
     const size_t ob = bi * os.b + h * os.h + s * os.s + lane * PER;
     if (dtype == BF16) {
       for (int e = 0; e < PER; ++e) ((__bf16*)out)[ob + e] = (__bf16)r[e];
@@ -57,10 +57,10 @@ __global__ __launch_bounds__(256) void merge_kernel(int rows, const float* __res
   if (lane == 0) lse_b[row] = lse;
 }
 
-hipError_t launch_merge(int rows, int d, const float* o_a, const float* lse_a, float* o_b, float* lse_b,
+hipError_t launch_merge(int64_t rows, int d, const float* o_a, const float* lse_a, float* o_b, float* lse_b,
                         void* out, Strides os, int hq, int sq, int dtype, hipStream_t st) {
   if (rows == 0) return hipSuccess;
-  const long blocks = ((long)rows * 32 + 255) / 256;   // one 32-lane group per row
+  const long blocks = (rows * 32 + 255) / 256;   // one 32-lane group per row (the caller checked the grid fits)
   if (d == 128)
     merge_kernel<128><<<(unsigned)blocks, 256, 0, st>>>(rows, o_a, lse_a, o_b, lse_b, out, os, hq, sq, dtype);
   else

@@ -126,7 +126,7 @@ struct TableJobs {
 };
 hipError_t launch_tile_ranges_batch(const TableJobs& jobs, hipStream_t st);
 hipError_t launch_docs_from_cu(const int* cu, int n_docs, int first, int n, int* doc, hipStream_t st);
-hipError_t launch_merge(int rows, int d, const float* o_a, const float* lse_a, float* o_b, float* lse_b,
+hipError_t launch_merge(int64_t rows, int d, const float* o_a, const float* lse_a, float* o_b, float* lse_b,
                         void* out, Strides os, int hq, int sq, int dtype, hipStream_t st);
 hipError_t launch_bwd_preprocess(int B, int hq, int sq, int d, const void* out, const void* d_o,
                                  Strides qs, int dtype, float* delta, hipStream_t st);

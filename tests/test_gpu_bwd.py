@@ -66,6 +66,74 @@ def test_bwd_rank_share_medium():
     _check(ring, inp, "causal")
 
 
+def test_bwd_causal_multi_chunk_work_list():
+    """Causal dK/dV workgroups whose work list (query head x 64-row tile) spans several chunks:
+    rank 0 of a 16384-token context over 2 zigzag shards, 4 query heads on 1 kv head, so each
+    key workgroup walks 4 x 128 = 512 items.  Every dQ, dK, dV element against the oracle."""
+    print_case("bwd: rank 0 of 2 zigzag shards, 16384 tokens, 4/1 heads, D=128 (512 work items per key tile)")
+    w = synthetic.small_workload("c4", seq=16384, n_shards=2, hq=4, hkv=1, seed=44)
+    pos = ra.sharding.shard_positions(w.seq, 2, "zigzag")
+    inp = synthetic.make_inputs(w, q_rows=pos[0])
+    ring = Ring(None, inp["k"], inp["v"], pos, "causal", "bf16", [0], q_shards=[inp["q"]], do_shards=[inp["do"]])
+    ring.forward().backward()
+    _check(ring, inp, "causal")
+
+
+def test_bwd_fp32_contiguous_ring_all_ranks():
+    """fp32 backward at the fp32 workload's shape (2 heads, D = 64, 512 tokens over 4 contiguous
+    shards, causal, all ranks): dQ, dK, dV max |err| <= 1e-5, the fp32 bound."""
+    print_case("bwd fp32: 4 contiguous ranks, 512 tokens, 2 heads, D=64, causal")
+    w = synthetic.small_workload("c1", backward=True)
+    inp = synthetic.make_inputs(w)
+    pos = ra.sharding.shard_positions(w.seq, w.n_shards, w.sharding)
+    ring = Ring(inp["q"], inp["k"], inp["v"], pos, "causal", "f32", range(4), do_glob=inp["do"])
+    ring.forward().backward()
+    s_all = np.arange(w.seq)
+    dQ, dK, dV = oracle.attention_backward(inp["q"], inp["k"], inp["v"], inp["do"], s_all, s_all, "causal")
+    for i, r in enumerate(ring.ranks):
+        e = max_abs(ring.numpy("dq")[i], dQ[:, :, pos[r]])
+        print(f"  rank {r}: dQ max abs {e:.3g}", flush=True)
+        assert e <= 1e-5
+    for n_, p in enumerate(pos):
+        ek, ev = max_abs(ring.numpy("dk")[n_], dK[:, :, p]), max_abs(ring.numpy("dv")[n_], dV[:, :, p])
+        print(f"  block {n_}: dK max abs {ek:.3g} dV max abs {ev:.3g}", flush=True)
+        assert ek <= 1e-5 and ev <= 1e-5
+
+
+@pytest.mark.parametrize("case", [("causal", 64, 1, 2, 1, 100, 150), ("none", 128, 2, 2, 2, 65, 70),
+                                  ("doc_causal", 64, 1, 4, 2, 130, 200), ("causal", 128, 1, 3, 1, 257, 190)],
+                         ids=lambda c: "-".join(map(str, c)))
+def test_step_bwd_fp32_ragged(case):
+    """fp32 backward step on ragged sizes with scattered positions and documents: max |err| <= 1e-5."""
+    mask, d, B, hq, hkv, sq, sk = case
+    print_case(f"step_bwd fp32 {case}")
+    rng = np.random.default_rng(sq * 7 + sk)
+    rnd = lambda *sh: rng.standard_normal(sh).astype(np.float32)
+    q, k, v, do = rnd(B, hq, sq, d), rnd(B, hkv, sk, d), rnd(B, hkv, sk, d), rnd(B, hq, sq, d)
+    perm = rng.permutation(sq + sk).astype(np.int32)
+    qp, kp = perm[:sq], perm[sq:]
+    docs = np.sort(rng.integers(0, 4, sq + sk)).astype(np.int32)
+    qd, kd = (docs[qp], docs[kp]) if mask == "doc_causal" else (None, None)
+    O, L = oracle.attention_forward(q, k, v, qp, kp, mask, qd, kd)
+    dQ, dK, dV = oracle.attention_backward(q, k, v, do, qp, kp, mask, qd, kd)
+    out = dev(O)
+    delta = torch.zeros(B, hq, sq, device="cuda")
+    ra.ringattn_bwd_preprocess(out, dev(do), delta)
+    dq = torch.zeros(B, hq, sq, d, device="cuda")
+    dk = torch.zeros(B, hkv, sk, d, device="cuda")
+    dv = torch.zeros(B, hkv, sk, d, device="cuda")
+    doc_t = (lambda x: None if x is None else dev(x, torch.int32))
+    ra.ringattn_step_bwd(dev(q), dev(k), dev(v), dev(do), dev(L), delta, dq, dk, dv, dev(qp, torch.int32),
+                         dev(kp, torch.int32), doc_t(qd), doc_t(kd),
+                         mask_mode={"none": ra.RA_MASK_NONE, "causal": ra.RA_MASK_CAUSAL,
+                                    "doc_causal": ra.RA_MASK_DOC_CAUSAL}[mask])
+    torch.cuda.synchronize()
+    for got, ref, name in ((dq, dQ, "dQ"), (dk, dK, "dK"), (dv, dV, "dV")):
+        e = max_abs(got.cpu().numpy(), ref)
+        print(f"  {name} max abs {e:.3g}", flush=True)
+        assert e <= 1e-5
+
+
 def test_bwd_doc_causal_thd_all_ranks():
     print_case("bwd: packed documents, THD layout, 4 contiguous shards of 8192 tokens, 8/2 heads")
     w = synthetic.small_workload("c5", seq=8192, n_shards=4, hq=8, hkv=2, seed=43)
@@ -157,6 +225,32 @@ def test_bwd_full_size_rank_share():
     assert e <= TOL
     for t in ring.dq + ring.dk + ring.dv:
         assert torch.isfinite(t).all()
+
+    # Element-wise dK/dV at full size: the same launch configuration again, with dO kept on a
+    # sample of rows of GQA group 0 (query heads 0-3) -- one random row of every 64-row query
+    # tile plus the chunk edges -- and zero everywhere else.  A row with dO = 0 has dP = 0 and
+    # delta = 0, so it adds exactly nothing to dQ, dK or dV; the oracle given only the sampled
+    # rows is then exact for every key of every block.  Other kv heads must stay exactly zero.
+    g = w.hq // w.hkv
+    tiles = pos[0].size // 64
+    local = np.unique(np.concatenate([np.arange(tiles) * 64 + rng.integers(0, 64, tiles), [0, c - 1, c, 2 * c - 1]]))
+    sparse = np.zeros_like(inp["do"])
+    sparse[:, :g, local] = inp["do"][:, :g, local]
+    ring.do = [dev(sparse, torch.bfloat16)]
+    print_case(f"c4 sparse dO: {local.size} rows of query heads 0-{g - 1}, backward again")
+    ring.backward()
+    _, dK, dV = oracle.attention_backward(inp["q"][:, :g, local], inp["k"][:, :1], inp["v"][:, :1],
+                                          inp["do"][:, :g, local], pos[0][local], np.arange(w.seq), "causal",
+                                          row_block=128, skip_masked_columns=True)
+    head0 = lambda t: t[:, :1].double().cpu().numpy()
+    for n_, p in enumerate(pos):
+        ek, ev = rel_l2(head0(ring.dk[n_]), dK[:, :, p]), rel_l2(head0(ring.dv[n_]), dV[:, :, p])
+        print(f"  block {n_}, kv head 0: dK rel L2 {ek:.3g} dV rel L2 {ev:.3g}", flush=True)
+        assert ek <= TOL and ev <= TOL
+        assert not ring.dk[n_][:, 1:].any() and not ring.dv[n_][:, 1:].any(), "kv heads without dO must stay zero"
+    others = torch.from_numpy(np.setdiff1d(np.arange(pos[0].size), local)).cuda()
+    dq = ring.dq[0]
+    assert not dq[:, g:].any() and not dq[:, :g].index_select(2, others).any(), "rows without dO must have dQ = 0"
 
 
 def test_c5_full_size_packed_documents():

@@ -91,9 +91,11 @@ def _sampled_rows(pos_rank, c, rng, n=48):
     return np.array(sorted(i for i in idx if 0 <= i < pos_rank.size))
 
 
-@pytest.mark.parametrize("rank", [0, 7])
+@pytest.mark.parametrize("rank", [0, 4, 7])
 def test_c3_full_size_one_rank_sampled_rows(rank):
-    """One rank's share of a 131072-token context over 8 zigzag blocks, prefetch on; exact per sampled row."""
+    """One rank's share of a 131072-token context over 8 zigzag blocks, prefetch on; exact per sampled row.
+
+    Ranks 0, N/2 and N-1: each holds a different mix of full, partial and empty tiles per step."""
     w = synthetic.WORKLOADS["c3"]
     print_case(f"c3: bf16 rank {rank} of 8, 16384 local queries, 8 steps of 16384 keys, zigzag causal")
     pos = ra.sharding.shard_positions(w.seq, w.n_shards, w.sharding)

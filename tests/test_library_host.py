@@ -243,3 +243,35 @@ def test_run_rejects_strided_blocks_and_missing_backward_buffers():
     assert _run(h, d) == _lib.RA_ERR_INVALID          # no d_o / delta / dq / dk / dv
     assert b"backward" in _lib.load().ringattn_last_error()
     assert h.untouched()
+
+
+def test_launch_size_limits():
+    """Problems whose launches would not fit one dispatch (grid work-items are 32-bit) are
+    rejected with RA_ERR_UNSUPPORTED before anything is enqueued; rows are never narrowed."""
+    lib = _lib.load()
+    h = Host()
+    # 2^27 rows of the standalone merge (one 32-lane group each): 2^32 work-items, one too many
+    p = _lib.RaProblem()
+    p.batch, p.hq, p.hkv, p.head_dim, p.sq, p.dtype = 1, 32, 32, 128, 1 << 22, _lib.RA_F32
+    assert lib.ringattn_merge(ctypes.byref(p), h.p("o"), h.p("lse"), h.p("dq"), h.p("delta"), None) \
+        == _lib.RA_ERR_UNSUPPORTED
+    assert b"merge" in lib.ringattn_last_error()
+    # beyond 2^31 rows the count would also wrap a 32-bit int: still rejected, not launched
+    p.batch, p.hq, p.sq = 4, 64, 1 << 24
+    assert lib.ringattn_merge(ctypes.byref(p), h.p("o"), h.p("lse"), h.p("dq"), h.p("delta"), None) \
+        == _lib.RA_ERR_UNSUPPORTED
+    # just inside the limit the merge passes validation (then fails on the misaligned pointer)
+    p.batch, p.hq, p.sq = 1, 32, (1 << 22) - 1
+    assert lib.ringattn_merge(ctypes.byref(p), h.p("o", 2), h.p("lse"), h.p("dq"), h.p("delta"), None) \
+        == _lib.RA_ERR_INVALID
+    # a step or ring whose forward, backward or merge grid would overflow
+    big = _problem(batch=64, hq=64, hkv=8, sq=1 << 20, sk=1024)
+    assert step_fwd(h, big) == _lib.RA_ERR_UNSUPPORTED
+    assert lib.ringattn_step_workspace_size(ctypes.byref(big)) == 0
+    d = _lib.RaRunDesc()
+    d.prob = big
+    d.n_ranks, d.n_emulated, d.mask_mode, d.pass_, d.flags = 8, 1, 1, _lib.RA_PASS_FWD, _lib.RA_RUN_MERGE_KERNEL
+    assert _run(h, d) == _lib.RA_ERR_UNSUPPORTED
+    # fp32 kernels run one wave per row: 2^26 rows is one dispatch too many
+    assert step_fwd(h, _problem(dtype=_lib.RA_F32, hq=64, hkv=64, sq=1 << 20)) == _lib.RA_ERR_UNSUPPORTED
+    assert h.untouched()
