@@ -144,6 +144,33 @@ int ringattn_step_fwd(const ra_problem* p, const void* q, const void* k_blk, con
                       int mask_mode, int flags, void* workspace, size_t workspace_bytes,
                       void* stream);
 
+/* Bytes of the device scratch array behind ringattn_step_fwd_noalloc (36 MiB per GPU). */
+#define RA_NOALLOC_SCRATCH_BYTES (36u << 20)
+
+/*
+ * ringattn_step_fwd without a workspace argument, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc).  Same arguments, results and errors as ringattn_step_fwd; the
+ * tile tables and the transposed value block go into a file-scope device array of
+ * RA_NOALLOC_SCRATCH_BYTES that each GPU holds from the library's first use of it on
+ * that device until the process ends.  The call allocates and frees nothing.
+ *   Limit: ringattn_step_workspace_size(p) <= RA_NOALLOC_SCRATCH_BYTES, else
+ *   RA_ERR_UNSUPPORTED (e.g. 16384-key blocks of 8 kv heads at D = 128 fit: 32 MiB of
+ *   transposed values; 32768-key blocks do not).
+ *   Device: the calling thread's current device, which must be the stream's
+ *   (RA_ERR_INVALID otherwise); its first call on a device looks up the array's
+ *   address there.
+ *   Concurrency: every call on one GPU shares that GPU's array.  Calls on one stream
+ *   are ordered; calls that overlap on one GPU (several streams, several threads)
+ *   race on it and give wrong results.  Nothing in the array has to start at zero:
+ *   each call writes every byte it reads.
+ */
+int ringattn_step_fwd_noalloc(const ra_problem* p, const void* q, const void* k_blk, const void* v_blk,
+                              float* o_acc, float* lse, void* out,
+                              const int32_t* q_pos, const int32_t* kv_pos,
+                              const int32_t* q_doc, const int32_t* kv_doc,
+                              int mask_mode, int flags, void* stream);
+
 /* Most K/V blocks one ringattn_fused_fwd call takes. */
 #define RA_FUSED_MAX_BLOCKS 16
 

@@ -23,10 +23,11 @@ from . import _lib
 from ._lib import (RA_BF16, RA_F32, RA_MASK_CAUSAL, RA_MASK_DOC_CAUSAL, RA_MASK_NONE, RA_MAX_SK, RA_NO_SKIP,
                    RA_PASS_BWD, RA_PASS_FWD, RA_RUN_ALLGATHER, RA_RUN_COPY_ENGINE, RA_RUN_MERGE_KERNEL,
                    RA_RUN_POISON, RA_RUN_SERIAL_COPY, RA_STEP_FIRST, RA_STEP_LAST, RA_FUSED_MAX_BLOCKS,
-                   RingAttnError)
+                   RA_NOALLOC_SCRATCH_BYTES, RingAttnError)
 from . import sharding
 
-__all__ = ["ringattn_step_workspace_size", "ringattn_step_fwd", "ringattn_fused_workspace_size",
+__all__ = ["ringattn_step_workspace_size", "ringattn_step_fwd", "ringattn_step_fwd_noalloc",
+           "ringattn_fused_workspace_size",
            "ringattn_fused_fwd", "ringattn_merge", "ringattn_bwd_preprocess",
            "ringattn_step_bwd", "ringattn_run_workspace_size", "ringattn_run", "ringattn_docs_from_cu_seqlens",
            "ringattn_last_error", "ringattn_version", "make_problem", "RingAttnError", "sharding",
@@ -34,7 +35,7 @@ __all__ = ["ringattn_step_workspace_size", "ringattn_step_fwd", "ringattn_fused_
            "RA_RUN_SERIAL_COPY", "RA_RUN_POISON", "RA_RUN_MERGE_KERNEL", "RA_RUN_COPY_ENGINE", "RA_RUN_ALLGATHER",
            "RA_FUSED_MAX_BLOCKS", "RA_PASS_FWD",
            "RA_PASS_BWD",
-           "RA_F32", "RA_BF16", "RA_MAX_SK"]
+           "RA_F32", "RA_BF16", "RA_MAX_SK", "RA_NOALLOC_SCRATCH_BYTES"]
 
 _DTYPES = {torch.float32: RA_F32, torch.bfloat16: RA_BF16}
 
@@ -112,6 +113,21 @@ def ringattn_step_fwd(q, k_blk, v_blk, o_acc, lse, out, q_pos, kv_pos, q_doc=Non
     return _lib.check(lib.ringattn_step_fwd(
         ctypes.byref(p), _ptr(q), _ptr(k_blk), _ptr(v_blk), _ptr(o_acc), _ptr(lse), _ptr(out), _ptr(q_pos),
         _ptr(kv_pos), _ptr(q_doc), _ptr(kv_doc), mask_mode, flags, _ptr(ws), ws.numel(), _stream(stream)))
+
+
+def ringattn_step_fwd_noalloc(q, k_blk, v_blk, o_acc, lse, out, q_pos, kv_pos, q_doc=None, kv_doc=None,
+                              mask_mode=RA_MASK_CAUSAL, flags=0, stream=None, softmax_scale=0.0):
+    """ringattn_step_fwd with the library's own device scratch instead of a workspace (no
+    allocation on any path: not here, not in the library); see the header for its limit."""
+    lib = _lib.load()
+    if v_blk.stride() != k_blk.stride() or v_blk.shape != k_blk.shape:
+        raise ValueError("k_blk and v_blk must have the same shape and strides")
+    if out is not None and out.stride() != q.stride():
+        raise ValueError("out must have the strides of q")
+    p = make_problem(q, k_blk, softmax_scale)
+    return _lib.check(lib.ringattn_step_fwd_noalloc(
+        ctypes.byref(p), _ptr(q), _ptr(k_blk), _ptr(v_blk), _ptr(o_acc), _ptr(lse), _ptr(out), _ptr(q_pos),
+        _ptr(kv_pos), _ptr(q_doc), _ptr(kv_doc), mask_mode, flags, _stream(stream)))
 
 
 def ringattn_fused_workspace_size(q: torch.Tensor, k: torch.Tensor, n_blocks: int) -> int:

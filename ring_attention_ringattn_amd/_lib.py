@@ -20,9 +20,11 @@ RA_RUN_SERIAL_COPY, RA_RUN_POISON, RA_RUN_MERGE_KERNEL, RA_RUN_COPY_ENGINE, RA_R
 RA_PASS_FWD, RA_PASS_BWD = 1, 2
 RA_MAX_SK = 262144
 RA_FUSED_MAX_BLOCKS = 16
+RA_NOALLOC_SCRATCH_BYTES = 36 << 20
 
 # every function include/ringattn.h declares
-EXPORTS = ("ringattn_step_workspace_size", "ringattn_step_fwd", "ringattn_fused_workspace_size", "ringattn_fused_fwd",
+EXPORTS = ("ringattn_step_workspace_size", "ringattn_step_fwd", "ringattn_step_fwd_noalloc",
+           "ringattn_fused_workspace_size", "ringattn_fused_fwd",
            "ringattn_merge", "ringattn_bwd_preprocess",
            "ringattn_step_bwd", "ringattn_run_workspace_size", "ringattn_run", "ringattn_docs_from_cu_seqlens",
            "ringattn_last_error", "ringattn_version")
@@ -49,6 +51,8 @@ _SIG = {
     "ringattn_step_workspace_size": (ctypes.c_size_t, [ctypes.POINTER(RaProblem)]),
     "ringattn_step_fwd": (_I, [ctypes.POINTER(RaProblem), _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _P,
                                ctypes.c_size_t, _P]),
+    "ringattn_step_fwd_noalloc": (_I, [ctypes.POINTER(RaProblem), _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I,
+                                       _P]),
     "ringattn_fused_workspace_size": (ctypes.c_size_t, [ctypes.POINTER(RaProblem), _I]),
     "ringattn_fused_fwd": (_I, [ctypes.POINTER(RaProblem), _I, _P, _PP, _PP, _P, _P, _P, _PP, _P, _PP, _I, _I, _P,
                                 ctypes.c_size_t, _P]),

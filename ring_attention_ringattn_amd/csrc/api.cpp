@@ -6,6 +6,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -206,6 +207,49 @@ hipError_t enqueue_bwd(const ra_problem* p, const BwdArgs& a, hipStream_t st) {
 
 const int kStepFlags = RA_STEP_FIRST | RA_STEP_LAST | RA_NO_SKIP;
 
+// Host validation of a forward step's arguments, all but the workspace (nothing is
+// checked past the descriptor, mask and flags when the query shard is empty).
+int check_step_fwd(const ra_problem* p, const void* q, const void* k_blk, const void* v_blk, const float* o_acc,
+                   const float* lse, const void* out, const int32_t* q_pos, const int32_t* kv_pos,
+                   const int32_t* q_doc, const int32_t* kv_doc, int mask_mode, int flags) {
+  if (int rc = check_problem(p)) return rc;
+  if (int rc = check_mask(mask_mode, q_doc, kv_doc, p->sk > 0)) return rc;
+  if (flags & ~kStepFlags) return fail(RA_ERR_INVALID, "unknown step flags 0x%x", flags);
+  if (p->sq == 0) return RA_OK;
+  if (int rc = check_ptr(q, "q")) return rc;
+  if (int rc = check_ptr(o_acc, "o_acc")) return rc;
+  if (int rc = check_ptr(lse, "lse", 4)) return rc;
+  if (int rc = check_ptr(q_pos, "q_pos", 4)) return rc;
+  if (p->sk > 0) {
+    if (int rc = check_ptr(k_blk, "k_blk")) return rc;
+    if (int rc = check_ptr(v_blk, "v_blk")) return rc;
+    if (int rc = check_ptr(kv_pos, "kv_pos", 4)) return rc;
+  }
+  if (out && !aligned(out, 16)) return fail(RA_ERR_INVALID, "out is not 16-byte aligned");
+  return RA_OK;
+}
+
+// Enqueue a validated forward step whose tile tables and transposed value block go
+// into `ws` (step_ws + vt_ws bytes, 16-byte aligned; every byte read is written first).
+int enqueue_step_fwd(const ra_problem* p, const void* q, const void* k_blk, const void* v_blk, float* o_acc,
+                     float* lse, void* out, const int32_t* q_pos, const int32_t* kv_pos, const int32_t* q_doc,
+                     const int32_t* kv_doc, int mask_mode, int flags, void* ws, hipStream_t st) {
+  const bool doc = mask_mode == RA_MASK_DOC_CAUSAL;
+  StepTables t = carve_step_ws(ws, p->sq);
+  hipError_t e = launch_tile_ranges(q_pos, doc ? q_doc : nullptr, p->sq, t.q, st);
+  if (e == hipSuccess) e = launch_tile_ranges(kv_pos, doc ? kv_doc : nullptr, p->sk, t.kv, st);
+  if (e != hipSuccess) return hip_fail(e, "tile-range kernel launch");
+  FwdArgs a = make_fwd(p, q, k_blk, v_blk, o_acc, lse, out, q_pos, kv_pos, q_doc, kv_doc, t.q, t.kv, mask_mode, flags);
+  if (vt_ws(p)) {
+    void* vt = (char*)ws + step_ws(p->sq, p->sk);
+    if ((e = transpose_v(p, v_blk, vt, st)) != hipSuccess) return hip_fail(e, "value transpose kernel launch");
+    a.vtb[0] = vt;
+  }
+  e = enqueue_fwd(p, a, st);
+  if (e != hipSuccess) return hip_fail(e, "forward step kernel launch");
+  return ok();
+}
+
 }  // namespace
 
 extern "C" {
@@ -223,40 +267,75 @@ int ringattn_step_fwd(const ra_problem* p, const void* q, const void* k_blk, con
                       float* lse, void* out, const int32_t* q_pos, const int32_t* kv_pos, const int32_t* q_doc,
                       const int32_t* kv_doc, int mask_mode, int flags, void* workspace, size_t workspace_bytes,
                       void* stream) {
-  if (int rc = check_problem(p)) return rc;
-  if (int rc = check_mask(mask_mode, q_doc, kv_doc, p->sk > 0)) return rc;
-  if (flags & ~kStepFlags) return fail(RA_ERR_INVALID, "unknown step flags 0x%x", flags);
+  if (int rc = check_step_fwd(p, q, k_blk, v_blk, o_acc, lse, out, q_pos, kv_pos, q_doc, kv_doc, mask_mode, flags))
+    return rc;
   if (p->sq == 0) return ok();
-  if (int rc = check_ptr(q, "q")) return rc;
-  if (int rc = check_ptr(o_acc, "o_acc")) return rc;
-  if (int rc = check_ptr(lse, "lse", 4)) return rc;
-  if (int rc = check_ptr(q_pos, "q_pos", 4)) return rc;
-  if (p->sk > 0) {
-    if (int rc = check_ptr(k_blk, "k_blk")) return rc;
-    if (int rc = check_ptr(v_blk, "v_blk")) return rc;
-    if (int rc = check_ptr(kv_pos, "kv_pos", 4)) return rc;
-  }
-  if (out && !aligned(out, 16)) return fail(RA_ERR_INVALID, "out is not 16-byte aligned");
   const size_t need = step_ws(p->sq, p->sk) + vt_ws(p);
   if (workspace_bytes < need || (need && !workspace))
     return fail(RA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, workspace_bytes);
   if (!aligned(workspace, 16)) return fail(RA_ERR_INVALID, "workspace is not 16-byte aligned");
+  return enqueue_step_fwd(p, q, k_blk, v_blk, o_acc, lse, out, q_pos, kv_pos, q_doc, kv_doc, mask_mode, flags,
+                          workspace, (hipStream_t)stream);
+}
 
-  hipStream_t st = (hipStream_t)stream;
-  const bool doc = mask_mode == RA_MASK_DOC_CAUSAL;
-  StepTables t = carve_step_ws(workspace, p->sq);
-  hipError_t e = launch_tile_ranges(q_pos, doc ? q_doc : nullptr, p->sq, t.q, st);
-  if (e == hipSuccess) e = launch_tile_ranges(kv_pos, doc ? kv_doc : nullptr, p->sk, t.kv, st);
-  if (e != hipSuccess) return hip_fail(e, "tile-range kernel launch");
-  FwdArgs a = make_fwd(p, q, k_blk, v_blk, o_acc, lse, out, q_pos, kv_pos, q_doc, kv_doc, t.q, t.kv, mask_mode, flags);
-  if (vt_ws(p)) {
-    void* vt = (char*)workspace + step_ws(p->sq, p->sk);
-    if ((e = transpose_v(p, v_blk, vt, st)) != hipSuccess) return hip_fail(e, "value transpose kernel launch");
-    a.vtb[0] = vt;
+}  // extern "C"
+
+// ------------------------------------------------------- allocation-free forward step
+// The workspace of ringattn_step_fwd_noalloc: a file-scope device array, one copy per GPU
+// (each device that loads the library holds its own, until the process ends).  In host
+// code its name is only a stand-in: the kernels get the per-device address that
+// hipGetSymbolAddress returns, taken once per device with that device current.
+static __device__ __align__(256) unsigned char scratch[RA_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Address of this device's `scratch` (device = the calling thread's current device, which
+// must be the one `stream` belongs to).
+int scratch_of_current_device(void* stream, void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(RA_ERR_UNSUPPORTED, "device %d: at most %d devices", dev, kMaxDevices);
+  if (stream) {
+    hipDevice_t sd = -1;
+    if ((e = hipStreamGetDevice((hipStream_t)stream, &sd)) != hipSuccess) return hip_fail(e, "hipStreamGetDevice");
+    if (sd != dev) return fail(RA_ERR_INVALID, "the stream belongs to device %d but device %d is current", (int)sd, dev);
   }
-  e = enqueue_fwd(p, a, st);
-  if (e != hipSuccess) return hip_fail(e, "forward step kernel launch");
-  return ok();
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    if ((e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch))) != hipSuccess)
+      return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return RA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int ringattn_step_fwd_noalloc(const ra_problem* p, const void* q, const void* k_blk, const void* v_blk, float* o_acc,
+                              float* lse, void* out, const int32_t* q_pos, const int32_t* kv_pos,
+                              const int32_t* q_doc, const int32_t* kv_doc, int mask_mode, int flags, void* stream) {
+  if (int rc = check_step_fwd(p, q, k_blk, v_blk, o_acc, lse, out, q_pos, kv_pos, q_doc, kv_doc, mask_mode, flags))
+    return rc;
+  if (p->sq == 0) return ok();
+  const size_t need = step_ws(p->sq, p->sk) + vt_ws(p);
+  if (need > RA_NOALLOC_SCRATCH_BYTES)
+    return fail(RA_ERR_UNSUPPORTED,
+                "this step needs %zu bytes of scratch (tile tables and the transposed value block); the "
+                "allocation-free entry point has %zu: use ringattn_step_fwd with a workspace",
+                need, (size_t)RA_NOALLOC_SCRATCH_BYTES);
+  void* ws = nullptr;
+  if (int rc = scratch_of_current_device(stream, &ws)) return rc;
+  return enqueue_step_fwd(p, q, k_blk, v_blk, o_acc, lse, out, q_pos, kv_pos, q_doc, kv_doc, mask_mode, flags, ws,
+                          (hipStream_t)stream);
 }
 
 size_t ringattn_fused_workspace_size(const ra_problem* p, int n_blocks) {

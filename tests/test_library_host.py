@@ -22,7 +22,7 @@ def declared_functions():
 
 def test_header_exports_match_library():
     names = declared_functions()
-    assert len(names) == 12, names
+    assert len(names) == 13, names
     assert sorted(_lib.EXPORTS) == names
     lib = _lib.load()
     for n in names:
@@ -274,4 +274,32 @@ def test_launch_size_limits():
     assert _run(h, d) == _lib.RA_ERR_UNSUPPORTED
     # fp32 kernels run one wave per row: 2^26 rows is one dispatch too many
     assert step_fwd(h, _problem(dtype=_lib.RA_F32, hq=64, hkv=64, sq=1 << 20)) == _lib.RA_ERR_UNSUPPORTED
+    assert h.untouched()
+
+
+def test_noalloc_step_rejects_what_its_scratch_cannot_hold():
+    """ringattn_step_fwd_noalloc validates exactly like ringattn_step_fwd, and a problem whose
+    tables and transposed value block exceed the scratch array is RA_ERR_UNSUPPORTED: all of it
+    host code, before any HIP call, outputs untouched."""
+    lib = _lib.load()
+    h = Host()
+
+    def call(p, **ptr):
+        a = dict(q=h.p("q"), k=h.p("k"), v=h.p("v"), o=h.p("o"), lse=h.p("lse"), out=h.p("out"), qp=h.p("qp"),
+                 kp=h.p("kp"))
+        a.update(ptr)
+        return lib.ringattn_step_fwd_noalloc(ctypes.byref(p), a["q"], a["k"], a["v"], a["o"], a["lse"], a["out"],
+                                             a["qp"], a["kp"], None, None, 1, 0, None)
+    # 32768-key blocks of 8 kv heads at D = 128: 64 MiB of transposed values
+    big = _problem(hq=32, hkv=8, sq=32768, sk=32768)
+    assert lib.ringattn_step_workspace_size(ctypes.byref(big)) > _lib.RA_NOALLOC_SCRATCH_BYTES
+    assert call(big) == _lib.RA_ERR_UNSUPPORTED
+    assert b"scratch" in lib.ringattn_last_error()
+    # the 16384-key blocks of the 131072-token share fit
+    fits = _problem(hq=32, hkv=8, sq=16384, sk=16384)
+    assert lib.ringattn_step_workspace_size(ctypes.byref(fits)) <= _lib.RA_NOALLOC_SCRATCH_BYTES
+    assert call(fits, q=None) == _lib.RA_ERR_INVALID          # the step's own checks come first
+    assert call(_problem(head_dim=96)) == _lib.RA_ERR_UNSUPPORTED
+    assert call(_problem(), kp=h.p("kp", 2)) == _lib.RA_ERR_INVALID
+    assert call(_problem(sq=0)) == _lib.RA_OK                 # empty shard: nothing to do
     assert h.untouched()
