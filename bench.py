@@ -1,25 +1,34 @@
 #!/usr/bin/env python3
 """Throughput of ring attention's per-device hot path on one MI355X.
 
-Workload (default): one rank's share of a 131072-token causal context sharded
-zigzag over 8 ranks -- 16384 local queries, 32 query heads over 8 key/value
-heads, head_dim 128, bf16 -- run as 8 ring steps, each against one
-16384-token key/value block, the next block copied device-to-device into a
-staging slot on a side stream while the current one computes.  One timed
-"step" is one whole ring (ringattn_run, forward with LSE) over resident
-inputs.  Optionally (--bwd) a second leg times forward+backward of the
-262144-token share (32768 local queries, 8 blocks of 32768 keys).
+Workload (the timed "step"): one rank's share of a 131072-token causal
+context sharded zigzag over 8 ranks -- 16384 local queries, 32 query heads
+over 8 key/value heads, head_dim 128, bf16 -- run as 8 ring steps, each
+against one 16384-token key/value block, the next block copied
+device-to-device into a staging slot on a side stream while the current one
+computes.  One timed step is one whole ring (ringattn_run, forward with LSE)
+over inputs resident in HBM.
+
+Legs reported beside it (same JSON line, `legs`): the same share with every
+block resident (all-gather rotation, one fused launch); the HBM-bound merge and
+backward preprocess; a matrix-core peak probe; the fp32 512-token ring (all 4
+ranks, in microseconds: launch-bound); the 8192-token zigzag ring (all 4
+ranks); forward+backward of the 262144-token share and of the 65536 packed
+document tokens.  `cpu_baseline`: the fp64 oracle on a bounded sample of the
+headline share (and the two small rings in full), on the host's cores.
 
 Throughput is causal-effective: FLOPs = 4 * D * Hq * P for the forward and
 10 * D * Hq * P for the backward, P = visible (query, key) pairs; skipped
 (masked) work is never counted.
 
 Prints one JSON line.  --gpus N > 1 is refused: this benchmark measures one
-GPU's share of the ring.
+GPU's share of the ring.  --summarize-trace turns a rocprofv3 kernel trace of
+this script into the markdown tables kept under profiles/.
 """
 from __future__ import annotations
 
 import argparse
+import contextlib
 import json
 import os
 import platform
@@ -31,9 +40,12 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA: 256 CUs x 4096 FLOP/clk x 2.4 GHz
 PEAK_HBM_GBS = 8000.0
+N_CU, BF16_FLOP_PER_CLK_CU = 256, 4096
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fwd_bf16_c3_traffic.json")
 KERNEL_SOURCES = ("ring_attention_ringattn_amd/csrc/fwd_bf16.hip", "ring_attention_ringattn_amd/csrc/mfma_tile.h",
                   "ring_attention_ringattn_amd/csrc/ra_internal.h")
+METRIC = "causal-effective attention TFLOP/s per rank-share (fwd, fwd+bwd); % bf16 MFMA peak"
+ALL_LEGS = ("allgather", "hbm", "mfma_peak", "c1", "c2", "c4", "c5")
 
 
 def kernel_source_hash():
@@ -69,7 +81,18 @@ def copy_calibration():
     torch.cuda.synchronize()
     print(json.dumps({"copy_calibration_bytes_read_per_copy": n * 4, "bytes_written_per_copy": n * 4,
                       "copies": 3}), flush=True)
-METRIC = "causal-effective attention TFLOP/s per rank-share (fwd, fwd+bwd); % bf16 MFMA peak"
+
+
+@contextlib.contextmanager
+def leg_range(name):
+    """A named range around a leg, so a kernel trace taken with markers can be split by leg."""
+    import torch
+    torch.cuda.nvtx.range_push(f"leg:{name}")
+    try:
+        yield
+    finally:
+        torch.cuda.synchronize()
+        torch.cuda.nvtx.range_pop()
 
 
 def visible_pairs(q_pos, kv_pos, docs=None):
@@ -89,26 +112,35 @@ def visible_pairs(q_pos, kv_pos, docs=None):
     return int(np.maximum(hi - lo, 0).sum())
 
 
-def setup_share(wname, ranks, with_bwd):
+def host_inputs(wname, ranks, with_bwd):
+    """Seeded host inputs of a ring: the listed (consecutive) ranks' query rows, every key and value."""
+    import numpy as np
+
+    import ring_attention_ringattn_amd as ra
+    import synthetic
+    w = synthetic.WORKLOADS[wname]
+    pos = ra.sharding.shard_positions(w.seq, w.n_shards, w.sharding)
+    q_rows = np.concatenate([pos[r] for r in ranks])
+    return w, pos, synthetic.make_inputs(w, q_rows=q_rows, backward=with_bwd)
+
+
+def setup_share(wname, ranks, with_bwd, host=None):
     """Device tensors of a ring: the listed (consecutive) ranks' query shards and all N home blocks."""
     import numpy as np
     import torch
 
     import ring_attention_ringattn_amd as ra
-    import synthetic
 
-    w = synthetic.WORKLOADS[wname]
+    w, pos, inp = host if host is not None else host_inputs(wname, ranks, with_bwd)
     n = w.n_shards
-    pos = ra.sharding.shard_positions(w.seq, n, w.sharding)
-    q_rows = np.concatenate([pos[r] for r in ranks])
-    inp = synthetic.make_inputs(w, q_rows=q_rows, backward=with_bwd)
-    bf = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda().to(torch.bfloat16)
+    dt = torch.float32 if w.dtype == "f32" else torch.bfloat16
+    cv = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda().to(dt)
     sl = lambda arr, i: arr[:, :, i * pos[0].size:(i + 1) * pos[0].size]
     s = {
-        "w": w, "n": n, "ranks": list(ranks), "pos": pos, "inp": inp,
-        "q": [bf(sl(inp["q"], i)) for i in range(len(ranks))],
-        "k": [bf(inp["k"][:, :, p]) for p in pos],
-        "v": [bf(inp["v"][:, :, p]) for p in pos],
+        "w": w, "n": n, "ranks": list(ranks), "pos": pos,
+        "q": [cv(sl(inp["q"], i)) for i in range(len(ranks))],
+        "k": [cv(inp["k"][:, :, p]) for p in pos],
+        "v": [cv(inp["v"][:, :, p]) for p in pos],
         "q_pos": [torch.from_numpy(pos[r]).cuda() for r in ranks],
         "kv_pos": [torch.from_numpy(p).cuda() for p in pos],
         "q_doc": None, "kv_doc": None,
@@ -119,11 +151,11 @@ def setup_share(wname, ranks, with_bwd):
         s["kv_doc"] = [ra.ringattn_docs_from_cu_seqlens(cu, int(p[0]), p.size) for p in pos]
         s["q_doc"] = [s["kv_doc"][r] for r in ranks]
     if with_bwd:
-        s["do"] = [bf(sl(inp["do"], i)) for i in range(len(ranks))]
+        s["do"] = [cv(sl(inp["do"], i)) for i in range(len(ranks))]
     shp = s["q"][0].shape
     s["o_acc"] = [torch.empty(shp, dtype=torch.float32, device="cuda") for _ in ranks]
     s["lse"] = [torch.empty(shp[:3], dtype=torch.float32, device="cuda") for _ in ranks]
-    s["out"] = [torch.empty(shp, dtype=torch.bfloat16, device="cuda") for _ in ranks]
+    s["out"] = [torch.empty(shp, dtype=dt, device="cuda") for _ in ranks]
     docs = None
     if inp["cu_seqlens"] is not None:
         cu_np = inp["cu_seqlens"]
@@ -171,6 +203,18 @@ def run_bwd(s, side):
                     copy_stream=side)
 
 
+def timed(fn, steps, warmup):
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        fn()
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) / steps
+
+
 def fwd_bwd_leg(name, ranks, side, steps, warmup, label):
     import torch
     s = setup_share(name, ranks, with_bwd=True)
@@ -186,6 +230,22 @@ def fwd_bwd_leg(name, ranks, side, steps, warmup, label):
             "fwd_tflops": round(fl_f / t_f / 1e12, 2), "bwd_tflops": round(fl_b / t_b / 1e12, 2),
             "fwd_bwd_tflops": round((fl_f + fl_b) / (t_f + t_b) / 1e12, 2),
             "fwd_bwd_pct_peak": round(100.0 * (fl_f + fl_b) / (t_f + t_b) / 1e12 / PEAK_BF16_TFLOPS, 2)}
+
+
+def fwd_ring_leg(name, side, steps, warmup, label):
+    """Forward ring of every rank of a small workload (all N ranks emulated in one ringattn_run)."""
+    import torch
+
+    import synthetic
+    w = synthetic.WORKLOADS[name]
+    s = setup_share(name, w.ranks(), with_bwd=False)
+    p = sum(s["pairs_per_step"])
+    t = timed(lambda: run_fwd(s, side), steps, warmup)
+    fl = 4.0 * w.head_dim * w.hq * w.batch * p
+    del s
+    torch.cuda.empty_cache()
+    return {"workload": label, "visible_pairs_per_head": p, "us_per_ring": round(t * 1e6, 1),
+            "fwd_tflops": round(fl / t / 1e12, 3), "pct_peak": round(100.0 * fl / t / 1e12 / PEAK_BF16_TFLOPS, 3)}
 
 
 def hbm_leg(steps, warmup):
@@ -205,21 +265,10 @@ def hbm_leg(steps, warmup):
     out, d_o = (torch.randn(B, H, S, D, device="cuda", generator=g).to(torch.bfloat16) for _ in range(2))
     delta = torch.empty(B, H, S, device="cuda")
 
-    def t(fn):
-        for _ in range(warmup):
-            fn()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for _ in range(steps):
-            fn()
-        e1.record()
-        torch.cuda.synchronize()
-        return e0.elapsed_time(e1) / steps / 1e3
-
     res = {}
     for name, fn, per_row in (("merge", lambda: ra.ringattn_merge(o_a, l_a, o_b, l_b), 3 * (4 * D + 4)),
                               ("bwd_preprocess", lambda: ra.ringattn_bwd_preprocess(out, d_o, delta), 4 * D + 4)):
-        sec = t(fn)
+        sec = event_time(fn, steps, warmup)
         nbytes = B * H * S * per_row
         res[name] = {"us": round(sec * 1e6, 2), "algorithmic_bytes": nbytes,
                      "gbs": round(nbytes / sec / 1e9, 1), "frac_of_hbm_peak": round(nbytes / sec / 1e9 / PEAK_HBM_GBS, 3)}
@@ -228,47 +277,213 @@ def hbm_leg(steps, warmup):
             **res}
 
 
-def timed(fn, steps, warmup):
+def event_time(fn, steps, warmup):
+    """Seconds per call of fn, from events on torch's current stream (where fn's kernels run)."""
     import torch
     for _ in range(warmup):
         fn()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
     for _ in range(steps):
         fn()
+    e1.record()
     torch.cuda.synchronize()
-    return (time.perf_counter() - t0) / steps
+    return e0.elapsed_time(e1) / steps / 1e3
 
 
-def cpu_baseline(w, inp, pos, budget_s):
-    """The fp64 oracle on a bounded sample of the same share: evenly spread query rows, all 32 heads."""
+def mfma_peak_leg(steps, warmup):
+    """Measured bf16 matrix-core throughput: back-to-back v_mfma_f32_32x32x16_bf16 on register
+    operands over every CU (libringattn_tools' probe kernel), beside the published peak."""
+    import ctypes
+
+    import torch
+    lib = ctypes.CDLL(os.path.join(ROOT, "ring_attention_ringattn_amd", "libringattn_tools.so"))
+    lib.ra_tool_mfma_peak.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    chains = lib.ra_tool_mfma_chains()
+    iters, blocks, threads = 4000, 4 * N_CU, 256
+    sink = torch.empty(blocks * threads, device="cuda")
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+    def launch():
+        if lib.ra_tool_mfma_peak(iters, blocks, threads, ctypes.c_void_p(sink.data_ptr()), stream) != 0:
+            raise RuntimeError("MFMA probe launch failed")
+    sec = event_time(launch, steps, warmup)
+    flop = blocks * (threads // 64) * iters * chains * 32 * 32 * 16 * 2
+    tf = flop / sec / 1e12
+    return {"workload": "matrix-core probe: back-to-back v_mfma_f32_32x32x16_bf16, register operands, "
+                        f"{blocks} workgroups of {threads // 64} waves, {iters * chains} products per wave",
+            "measured_tflops": round(tf, 1), "spec_tflops": PEAK_BF16_TFLOPS,
+            "frac_of_spec": round(tf / PEAK_BF16_TFLOPS, 4),
+            "implied_clock_ghz": round(tf * 1e12 / (N_CU * BF16_FLOP_PER_CLK_CU) / 1e9, 3)}
+
+
+# ------------------------------------------------------------------ CPU baseline (fp64 oracle)
+
+_CPU = {}   # host inputs the forked workers read (set before the pool starts)
+
+
+def _cpu_worker_init():
+    from threadpoolctl import threadpool_limits
+    _CPU["limits"] = threadpool_limits(limits=1)   # one BLAS thread per process
+
+
+def _cpu_task(task):
+    """The oracle forward of a few query rows of one head against every visible key."""
     import numpy as np
 
     import oracle
+    wname, h, rows = task
+    w, pos_rows, inp = _CPU[wname]
+    kvh = h * w.hkv // w.hq
+    oracle.attention_forward(inp["q"][:, h:h + 1, rows], inp["k"][:, kvh:kvh + 1], inp["v"][:, kvh:kvh + 1],
+                             pos_rows[rows], np.arange(w.seq), "causal", row_block=128,
+                             skip_masked_columns=True)
+    return int((pos_rows[rows] + 1).sum())   # visible keys of a causal row at position p: p + 1
+
+
+def _host_facts():
+    import numpy as np
+    model = platform.processor() or platform.machine()
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
     try:
         from threadpoolctl import threadpool_info
-        threads = max([p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"] or [1])
+        blas = ", ".join(sorted({f"{p.get('internal_api')} {p.get('version')}" for p in threadpool_info()
+                                 if p.get("user_api") == "blas"})) or "unknown"
     except Exception:
-        threads = 1
-    kpos = np.arange(w.seq)
-    done_rows, done_pairs, spent = 0, 0, 0.0
-    n_rows = 4
+        blas = "unknown"
+    return model, np.__version__, blas
+
+
+def cpu_baseline(c3_host, budget_s):
+    """The fp64 oracle, as it stands, on the host's cores: a fork pool of one-BLAS-thread
+    processes over (head, 8 query rows) tasks.  Headline: a bounded sample of the 131072-token
+    share (per head 64 seeded random rows plus the zigzag chunk edges, all visible keys), for at
+    most `budget_s` seconds of wall time; beside it the 512-token fp32 ring and the 8192-token
+    ring in full.  Runs before the GPU is touched (forking then is safe)."""
+    import multiprocessing
+
+    import numpy as np
+
+    import synthetic
+    _CPU.clear()
+    wc, _, inpc = c3_host
+    rows_pos = np.asarray(inpc["q_rows"])
+    _CPU["c3"] = (wc, rows_pos, inpc)
+    small = {}
+    for name in ("c1", "c2"):
+        w, _, inp = host_inputs(name, synthetic.WORKLOADS[name].ranks(), False)
+        _CPU[name] = (w, np.asarray(inp["q_rows"]), inp)
+        small[name] = w
+    workers = max(1, min(16, len(os.sched_getaffinity(0))))
     rng = np.random.default_rng(0)
-    while spent < budget_s and done_rows < pos.size:
-        idx = np.sort(rng.choice(pos.size, n_rows, replace=False))
-        t0 = time.perf_counter()
-        oracle.attention_forward(inp["q"][:, :, idx], inp["k"], inp["v"], pos[idx], kpos, "causal",
-                                 row_block=128, skip_masked_columns=True)
-        spent += time.perf_counter() - t0
-        done_rows += n_rows
-        done_pairs += visible_pairs(pos[idx], kpos)
-        n_rows = min(64, n_rows * 2)
-    flops = 4.0 * w.head_dim * w.hq * w.batch * done_pairs
-    return {"value": flops / spent / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"fp64 oracle forward of {done_rows} query rows of the same rank share (all {w.hq} heads, "
-                      f"all visible keys of the 131072-token context), {spent:.1f} s, "
-                      f"{done_pairs} visible pairs per head; host {platform.processor() or platform.machine()}, "
-                      f"{len(os.sched_getaffinity(0))} cores available"}
+    c = wc.seq // (2 * wc.n_shards)
+    n_local = rows_pos.size
+    tasks = {}
+    for h in range(wc.hq):
+        rows = np.unique(np.concatenate([rng.choice(n_local, 64, replace=False), [0, c - 1, c, 2 * c - 1]]))
+        tasks.setdefault("c3", []).extend(("c3", h, rows[i:i + 8]) for i in range(0, rows.size, 8))
+    for name, w in small.items():
+        n = _CPU[name][1].size
+        tasks[name] = [(name, h, np.arange(i, min(n, i + 64))) for i in range(0, n, 64) for h in range(w.hq)]
+    model, npver, blas = _host_facts()
+    ctx = multiprocessing.get_context("fork")
+    res = {}
+    with ctx.Pool(workers, initializer=_cpu_worker_init) as pool:
+        for name in ("c3", "c1", "c2"):
+            w = _CPU[name][0]
+            done = pairs = 0
+            t0 = time.perf_counter()
+            for p in pool.imap_unordered(_cpu_task, tasks[name]):
+                pairs += p
+                done += 1
+                if name == "c3" and time.perf_counter() - t0 > budget_s:
+                    break
+            sec = time.perf_counter() - t0
+            res[name] = (done, len(tasks[name]), pairs, sec, 4.0 * w.head_dim * pairs / sec / 1e12)
+        pool.terminate()
+    done, total, pairs, sec, tf = res["c3"]
+    return {"value": round(tf, 5), "unit": "TFLOP/s", "cores": workers, "kind": "oracle",
+            "sample": f"fp64 oracle forward (numpy) of {done} of {total} tasks of the 131072-token rank share: "
+                      f"per head 64 seeded random query rows plus the zigzag chunk edges, 8 rows x 1 head per "
+                      f"task, all visible keys; {pairs} visible (row, key) pairs over the sampled heads in "
+                      f"{sec:.1f} s wall; a fork pool of {workers} processes with one BLAS thread each; "
+                      f"host CPU {model}; numpy {npver}; BLAS {blas}",
+            "per_config": {
+                name: {"workload": label, "tasks": f"{res[name][0]} of {res[name][1]}", "seconds": round(res[name][3], 2),
+                       "tflops": round(res[name][4], 5)}
+                for name, label in (("c1", "fp32 512-token ring, full forward of all 4 ranks (2 heads, D = 64)"),
+                                    ("c2", "8192-token zigzag ring, full forward of all 4 ranks (32/8 heads, "
+                                           "D = 128)"))}}
+
+
+# ------------------------------------------------------------------ trace summaries (profiles/)
+
+def _demangle(name):
+    import re
+    n = re.sub(r"\(.*", "", name).replace("void ", "")
+    return {"_ZN2ra19vt_transpose_kernelILi128EEEvPKDF16bNS_7StridesEiiiPDF16b": "ra::vt_transpose_kernel<128>",
+            "_ZN2ra14bwd_pre_kernelILi128EDF16bEEviiiPKT0_S3_NS_7StridesEPf": "ra::bwd_pre_kernel<128, bf16>"}.get(n, n)
+
+
+def summarize_trace(trace_dir, bench_log):
+    """Markdown summary of a rocprofv3 kernel trace of this script.  With a marker trace beside it
+    (legs run inside named ranges), launches are grouped by leg; the headline ring's forward step
+    launches of the timed rings (the last steps x 8 of that leg) are summarised on their own, with
+    the roofline fraction they give."""
+    import csv
+    import glob
+    import re
+    line = [l for l in open(bench_log).read().splitlines() if l.startswith("{")][-1]
+    bench = json.loads(line)
+    kt = glob.glob(os.path.join(trace_dir, "**", "*kernel_trace.csv"), recursive=True)[0]
+    rows = sorted(csv.DictReader(open(kt)), key=lambda r: int(r["Start_Timestamp"]))
+    ranges = []
+    mk = glob.glob(os.path.join(trace_dir, "**", "*marker_api_trace.csv"), recursive=True)
+    if mk:
+        for r in csv.DictReader(open(mk[0])):
+            msg = r.get("Message") or r.get("Marker_Message") or r.get("Function") or ""
+            if msg.startswith("leg:"):
+                ranges.append((int(r["Start_Timestamp"]), int(r["End_Timestamp"]), msg[4:]))
+
+    def leg_of(ts):
+        for a, b, n in ranges:
+            if a <= ts <= b:
+                return n
+        return "c3_ring" if ranges else "-"
+    agg = {}
+    step = []
+    for r in rows:
+        n = _demangle(r["Kernel_Name"])
+        if not (n.startswith("ra::") or n.startswith("__amd_rocclr_copyBuffer")):
+            continue
+        leg = leg_of(int(r["Start_Timestamp"]))
+        dur = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+        agg.setdefault((leg, n, int(r["Grid_Size_X"]), int(r["Workgroup_Size_X"])), []).append(dur)
+        if leg in ("c3_ring", "-") and n.startswith("ra::fwd_bf16_kernel<128, false>"):
+            step.append(dur)
+    out = ["| leg | kernel | grid (threads) | block | launches | avg us | min us | max us |",
+           "|---|---|---|---|---|---|---|---|"]
+    for (leg, n, g, b), d in sorted(agg.items(), key=lambda kv: (kv[0][0], -sum(kv[1]))):
+        out.append(f"| {leg} | `{n}` | {g} | {b} | {len(d)} | {sum(d) / len(d):.1f} | {min(d):.1f} | {max(d):.1f} |")
+    k, nsteps = bench["steps"], bench["config"]["ring_steps"]
+    timed_steps = step[-k * nsteps:]
+    flops = bench["roofline"]["flop_per_launch"]
+    tf = sum(flops) * k / (sum(timed_steps) / 1e6) / 1e12 if timed_steps else float("nan")
+    per_step = [sum(timed_steps[t::nsteps]) / k for t in range(nsteps)] if timed_steps else []
+    head = [
+        f"Headline forward step kernel `ra::fwd_bf16_kernel<128, false>`, the {k} timed rings ({k * nsteps} "
+        f"launches, after {bench['warmup']} warm-up rings): average {sum(timed_steps) / len(timed_steps):.1f} us per "
+        f"launch; per ring step (us) {[round(x, 1) for x in per_step]}; {tf:.1f} TFLOP/s over the causal-effective "
+        f"FLOPs of those launches, frac {tf / PEAK_BF16_TFLOPS:.4f} of {PEAK_BF16_TFLOPS} (the bench line of the same "
+        f"run: roofline frac {bench['roofline']['frac']}, {bench['ms_per_step']} ms per ring; 8 x average launch = "
+        f"{8 * sum(timed_steps) / len(timed_steps) / 1e3:.3f} ms).", ""]
+    return "\n".join(head + out) + "\n\nThe bench line of this run:\n\n    " + line + "\n"
 
 
 def main():
@@ -279,33 +494,47 @@ def main():
                     help="untimed rings first: under sustained load the shader clock settles "
                          "(about 1.5 -> 1.84 GHz on MI355X) within the first ~50 ms")
     ap.add_argument("--rank", type=int, default=0)
-    ap.add_argument("--no-bwd", action="store_true", help="skip the forward+backward legs")
+    ap.add_argument("--legs", default=",".join(ALL_LEGS),
+                    help=f"comma-separated legs to run beside the headline ring (of {','.join(ALL_LEGS)}; '' for none)")
+    ap.add_argument("--no-bwd", action="store_true", help="skip the forward+backward legs (c4, c5)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for the CPU baseline")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 256 MiB device copy (for scaling HBM byte counters)")
+    ap.add_argument("--summarize-trace", nargs=2, metavar=("TRACE_DIR", "BENCH_LOG"),
+                    help="print the markdown summary of a rocprofv3 trace of this script and exit (no GPU)")
     args = ap.parse_args()
+    if args.summarize_trace:
+        print(summarize_trace(*args.summarize_trace), end="")
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU's share of the ring; --gpus {args.gpus} is not supported "
               "(this build runs on a single MI355X and emulates the ring's ranks on it)", file=sys.stderr)
         sys.exit(2)
-
     if args.copy_calibration:
         copy_calibration()
         return
+    legs = [x for x in args.legs.split(",") if x]
+    if args.no_bwd:
+        legs = [x for x in legs if x not in ("c4", "c5")]
+    unknown = set(legs) - set(ALL_LEGS)
+    if unknown:
+        ap.error(f"unknown legs {sorted(unknown)}")
+
+    # host inputs of the headline share, and the CPU baseline, before anything touches the GPU
+    host = host_inputs("c3", [args.rank], False)
+    cpu = None if args.no_cpu_baseline else cpu_baseline(host, args.cpu_budget)
 
     import torch
-    import ring_attention_ringattn_amd as ra
-
     torch.cuda.set_device(0)
-    s = setup_share("c3", [args.rank], with_bwd=False)
+    s = setup_share("c3", [args.rank], with_bwd=False, host=host)
+    del host
     side = torch.cuda.Stream()
     n = s["n"]
     w = s["w"]
     flops_step = [4.0 * w.head_dim * w.hq * w.batch * p for p in s["pairs_per_step"]]
     flops_ring = sum(flops_step)
 
-    host = (w, s["inp"], s["pos"][args.rank])   # kept for the CPU baseline
     # Events around every step of every timed ring, recorded on the compute stream inside the
     # timed region: their spans are the step kernel's launch durations.
     ev_sets = [[torch.cuda.Event(enable_timing=True) for _ in range(2 * n)] for _ in range(args.steps)]
@@ -313,14 +542,15 @@ def main():
         for e in es:
             e.record()        # creates the underlying hipEvent_t
     handles = [[e.cuda_event for e in es] for es in ev_sets]
-    for _ in range(args.warmup):
-        run_fwd(s, side)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        run_fwd(s, side, handles[i])
-    torch.cuda.synchronize()
-    t_ring = (time.perf_counter() - t0) / args.steps
+    with leg_range("c3_ring"):
+        for _ in range(args.warmup):
+            run_fwd(s, side)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            run_fwd(s, side, handles[i])
+        torch.cuda.synchronize()
+        t_ring = (time.perf_counter() - t0) / args.steps
     kern_ms = [sum(es[2 * t].elapsed_time(es[2 * t + 1]) for es in ev_sets) / args.steps for t in range(n)]
     achieved = flops_ring / (sum(kern_ms) / 1e3) / 1e12
 
@@ -351,34 +581,52 @@ def main():
                      "kernel": "ra::fwd_bf16_kernel<128,*>",
                      "per_launch_ms": [round(x, 4) for x in kern_ms],
                      "flop_per_launch": flops_step},
+        "legs": {},
     }
 
-    # the all-gather rotation on the same share: every block resident, one fused launch
-    t_ag = timed(lambda: run_fwd_allgather(s), args.steps, args.warmup)
-    result["legs"] = {"fwd_allgather_131072_rank_share": {
-        "workload": "the same rank share with all 8 K/V blocks resident (all-gather rotation): one fused "
-                    "launch over every block, softmax state kept in registers, no ring steps",
-        "fwd_ms": round(t_ag * 1e3, 3), "fwd_tflops": round(flops_ring / t_ag / 1e12, 2),
-        "pct_peak": round(100.0 * flops_ring / t_ag / 1e12 / PEAK_BF16_TFLOPS, 2)}}
-
-    result["legs"]["hbm_kernels_131072_rank_share"] = hbm_leg(max(args.steps, 20), args.warmup)
-
-    if not args.no_bwd:
-        del s
-        torch.cuda.empty_cache()
-        result["legs"].update({
-            "fwd_bwd_262144_rank_share": fwd_bwd_leg(
+    if "allgather" in legs:
+        with leg_range("allgather"):
+            t_ag = timed(lambda: run_fwd_allgather(s), args.steps, args.warmup)
+        result["legs"]["fwd_allgather_131072_rank_share"] = {
+            "workload": "the same rank share with all 8 K/V blocks resident (all-gather rotation): one fused "
+                        "launch over every block, softmax state kept in registers, no ring steps",
+            "fwd_ms": round(t_ag * 1e3, 3), "fwd_tflops": round(flops_ring / t_ag / 1e12, 2),
+            "pct_peak": round(100.0 * flops_ring / t_ag / 1e12 / PEAK_BF16_TFLOPS, 2)}
+    del s
+    torch.cuda.empty_cache()
+    if "hbm" in legs:
+        with leg_range("hbm"):
+            result["legs"]["hbm_kernels_131072_rank_share"] = hbm_leg(max(args.steps, 20), args.warmup)
+    if "mfma_peak" in legs:
+        with leg_range("mfma_peak"):
+            result["legs"]["mfma_peak_probe"] = mfma_peak_leg(5, 2)
+    if "c1" in legs:
+        with leg_range("c1"):
+            result["legs"]["fwd_fp32_512_all_ranks"] = fwd_ring_leg(
+                "c1", side, max(args.steps, 20), args.warmup,
+                "fp32, 2 heads (MHA), D = 64, 512 tokens over 4 contiguous ring shards, causal, all 4 ranks "
+                "emulated in one ring (launch-bound: reported in microseconds)")
+    if "c2" in legs:
+        with leg_range("c2"):
+            result["legs"]["fwd_8192_zigzag_all_ranks"] = fwd_ring_leg(
+                "c2", side, max(args.steps, 20), args.warmup,
+                "bf16, 32/8 heads, D = 128, 8192 tokens over 4 zigzag ring shards of 2048, causal, all 4 ranks "
+                "emulated in one ring")
+    if "c4" in legs:
+        with leg_range("c4"):
+            result["legs"]["fwd_bwd_262144_rank_share"] = fwd_bwd_leg(
                 "c4", [args.rank], side, args.steps, args.warmup,
                 "rank share of a 262144-token causal context over 8 zigzag shards (32768 local queries, "
-                "8 steps of 32768-token blocks), 32/8 heads, D=128, bf16, forward + backward"),
-            "fwd_bwd_packed_documents": fwd_bwd_leg(
+                "8 steps of 32768-token blocks), 32/8 heads, D=128, bf16, forward + backward")
+    if "c5" in legs:
+        with leg_range("c5"):
+            result["legs"]["fwd_bwd_packed_documents"] = fwd_bwd_leg(
                 "c5", [0, 1, 2, 3], side, args.steps, args.warmup,
                 "65536 packed tokens of lognormal documents (seed 5: 22 documents), document-causal, "
-                "4 contiguous ring shards, all ranks, 32/8 heads, D=128, bf16, forward + backward"),
-        })
+                "4 contiguous ring shards, all ranks, 32/8 heads, D=128, bf16, forward + backward")
 
-    if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(*host, args.cpu_budget)
+    if cpu is not None:
+        result["cpu_baseline"] = cpu
     print(json.dumps(result), flush=True)
 
 

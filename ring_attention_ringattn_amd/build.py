@@ -14,6 +14,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libringattn.so")
+TOOLS = os.path.join(CSRC, "tools")
+TOOLS_LIB = os.path.join(PKG, "libringattn_tools.so")   # measurement probes for the benchmark
 ARCH = os.environ.get("RINGATTN_ARCH", "gfx950")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -23,8 +25,8 @@ FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-I", os.path.j
          "-Wall", "-Wno-unused-variable", "-Wno-unused-function"]
 
 
-def sources():
-    return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith((".hip", ".cpp")))
+def sources(folder=CSRC):
+    return sorted(os.path.join(folder, f) for f in os.listdir(folder) if f.endswith((".hip", ".cpp")))
 
 
 def _compile(src, extra=(), build_dir=BUILD):
@@ -39,12 +41,18 @@ def _compile(src, extra=(), build_dir=BUILD):
     return obj, errs
 
 
-def build(verbose: bool = False, out: str = LIB, defines=(), build_dir: str = BUILD) -> str:
-    """Compile every source and link ``out``; ``defines`` are extra -D flags (tuning variants)."""
+def build(verbose: bool = False, out: str = LIB, defines=(), build_dir: str = BUILD, with_tools: bool = True) -> str:
+    """Compile every source and link ``out`` (and the benchmark's probe library unless
+    ``with_tools`` is false); ``defines`` are extra -D flags (tuning variants)."""
+    if with_tools:
+        _link(sources(TOOLS), TOOLS_LIB, [], os.path.join(build_dir, "tools"), verbose)
+    return _link(sources(), out, [f"-D{d}" for d in defines], build_dir, verbose)
+
+
+def _link(srcs, out, extra, build_dir, verbose):
     os.makedirs(build_dir, exist_ok=True)
-    extra = [f"-D{d}" for d in defines]
     with cf.ThreadPoolExecutor(max_workers=min(8, os.cpu_count() or 4)) as ex:
-        results = list(ex.map(lambda s: _compile(s, extra, build_dir), sources()))
+        results = list(ex.map(lambda s: _compile(s, extra, build_dir), srcs))
     for _, errs in results:
         if verbose and errs.strip():
             print(errs, file=sys.stderr)

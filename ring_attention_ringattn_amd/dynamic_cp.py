@@ -10,14 +10,21 @@ simulator, belongs to pipeline parallelism and is not built here.
 
 The page gives no formulas; the readings taken here:
 
-* Cost of one micro-batch (documents d_1..d_k packed in THD form, document-
-  causal attention, context-parallel size c, per rank):
-      T = (alpha * sum d_i^2 + beta * sum d_i) / c + eps * sum d_i + gamma * c + delta
-  the quadratic and linear attention terms split over c ranks; eps for the work
-  every ring step repeats on the rank's running output (c steps over n/c rows:
-  n rows whatever c is); gamma per ring step (c steps) and a fixed delta.  The
-  coefficients are fitted by least squares to timings of this library's own
-  kernels (`measure`).
+* Cost of one micro-batch (documents d_1..d_k packed in THD form in that order,
+  document-causal attention, split contiguously over a ring of c ranks):
+      T = alpha * P_crit + beta * sum d_i / c + eps * sum d_i + gamma * c + delta
+  P_crit is the attention work on the ring's critical path: every ring step
+  ends when its slowest rank does, so P_crit = sum over steps t of the largest,
+  over ranks r, count of visible (query, key) pairs between rank r's queries and
+  the block it holds at step t (`step_pairs`, exact, from the document
+  boundaries).  For balanced work it is the quadratic sum d_i^2 / (2c) the page
+  speaks of; for one long document split contiguously the last rank does
+  (2c - 1) / c times the mean, and P_crit charges that.  beta: linear work split
+  over c; eps: the work every ring step repeats on the rank's running output
+  (c steps over n/c rows: n rows whatever c is); gamma per ring step (c steps)
+  and a fixed delta.  The coefficients are fitted by least squares to timings
+  of this library's own kernels (`measure`), each micro-batch timed the same
+  way: the sum over steps of its slowest rank's step time.
 * Memory limit: at most `tokens_per_gpu` tokens of a micro-batch per GPU, so a
   micro-batch of n tokens needs c >= n / tokens_per_gpu; c is a power of two
   up to the number of GPUs (the page builds CP groups of power-of-two sizes).
@@ -41,18 +48,57 @@ from typing import List, Sequence, Tuple
 import numpy as np
 
 
+TILE = 64   # a ring rank holds whole 64-token tiles; a micro-batch is padded to that
+
+
+def ring_docs(docs: Sequence[int], cp: int) -> List[int]:
+    """The documents of a micro-batch as its ring runs them: one extra padding document
+    makes the packed stream a whole number of 64-token tiles per rank."""
+    pad = (-int(sum(docs))) % (TILE * cp)
+    return [int(x) for x in docs] + ([pad] if pad else [])
+
+
+def step_pairs(docs: Sequence[int], cp: int) -> np.ndarray:
+    """[cp, cp] int64: visible (query, key) pairs of rank r's queries against the block it
+    holds at ring step t, block (r - t) mod cp (document-causal; the padded stream split
+    contiguously).  For queries i in [qa, qb) and keys [ka, ka + L) of one document, the
+    count is sum_i clamp(i - ka + 1, 0, L), a difference of two closed-form prefix sums."""
+    d = np.asarray(ring_docs(docs, cp), dtype=np.int64)
+    ends = np.cumsum(d)
+    starts = ends - d
+    s = int(ends[-1]) // cp
+    r = np.arange(cp)[:, None, None]
+    t = np.arange(cp)[None, :, None]
+    j = (r - t) % cp
+    qa, qb = np.maximum(starts, r * s), np.minimum(ends, (r + 1) * s)
+    ka, kb = np.maximum(starts, j * s), np.minimum(ends, (j + 1) * s)
+    L = np.maximum(kb - ka, 0)
+
+    def prefix(x):   # sum over queries i < x of the keys of [ka, ka + L) at or before i
+        m = np.maximum(x - ka, 0)
+        inside = np.minimum(m, L)
+        return inside * (inside + 1) // 2 + np.maximum(m - L, 0) * L
+    pairs = np.where(qb > qa, prefix(qb) - prefix(qa), 0)
+    return pairs.sum(axis=2)
+
+
+def critical_pairs(docs: Sequence[int], cp: int) -> int:
+    """Attention pairs on the ring's critical path: each step waits for its slowest rank."""
+    return int(step_pairs(docs, cp).max(axis=0).sum())
+
+
 @dataclasses.dataclass(frozen=True)
 class CostModel:
-    alpha: float    # ms per (token^2) of attention work, per rank before the split over c
+    alpha: float    # ms per visible (query, key) pair on the critical path (all heads)
     beta: float     # ms per token, split over c
     eps: float      # ms per token of the micro-batch, not split (per-step running output)
     gamma: float    # ms per ring step
     delta: float    # ms fixed
 
     def predict(self, docs: Sequence[int], cp: int) -> float:
-        d = np.asarray(docs, dtype=np.float64)
-        return float((self.alpha * np.sum(d * d) + self.beta * np.sum(d)) / cp + self.eps * np.sum(d)
-                     + self.gamma * cp + self.delta)
+        n = float(sum(docs))
+        return float(self.alpha * critical_pairs(docs, cp) + self.beta * n / cp + self.eps * n + self.gamma * cp
+                     + self.delta)
 
 
 def fit_cost_model(samples: Sequence[Tuple[Sequence[int], int, float]]) -> Tuple[CostModel, float]:
@@ -61,8 +107,8 @@ def fit_cost_model(samples: Sequence[Tuple[Sequence[int], int, float]]) -> Tuple
     and the largest relative error over the samples."""
     rows, y = [], []
     for docs, cp, ms in samples:
-        d = np.asarray(docs, dtype=np.float64)
-        rows.append([np.sum(d * d) / cp, np.sum(d) / cp, np.sum(d), cp, 1.0])
+        n = float(sum(docs))
+        rows.append([critical_pairs(docs, cp), n / cp, n, cp, 1.0])
         y.append(ms)
     a, y = np.asarray(rows), np.asarray(y)
     w = 1.0 / y
@@ -241,20 +287,29 @@ def lognormal_lengths(seed: int, n: int, median: float = 2048.0, sigma: float = 
 
 # ------------------------------------------------------------------ measurement (GPU)
 
+@dataclasses.dataclass
+class RingTiming:
+    ms: float                 # forward + backward of the ring: per step, its slowest rank
+    per_rank_ms: List[float]  # each rank's own forward + backward ring
+
+
 def time_micro_batch(docs: Sequence[int], cp: int, hq: int = 32, hkv: int = 8, d: int = 128, reps: int = 5,
-                     seed: int = 0) -> float:
-    """Per-rank milliseconds of forward + backward attention of one packed micro-batch
-    (documents `docs`, document-causal) over a ring of `cp` ranks: all `cp` ranks are run
-    on this GPU by the library's ring driver, and the time (median over `reps` runs) is
-    divided by `cp`."""
+                     seed: int = 0) -> RingTiming:
+    """Forward + backward attention of one packed micro-batch (documents `docs`, document-
+    causal, contiguous shards) on a ring of `cp` ranks, as a real ring would take it.
+
+    Every rank runs alone on this GPU through the library's ring driver (one emulated rank
+    per call), with events around each of its ring steps and around the whole call.  A ring
+    step ends when its slowest rank does, so the ring's time is the sum over steps of the
+    largest step time over ranks, plus the largest per-rank time outside the steps (tile
+    tables, backward preprocess, launch gaps); forward and backward each.  Each (rank,
+    step) time is the median over `reps` runs."""
     import torch
     import ring_attention_ringattn_amd as ra
     from . import sharding
 
+    docs = ring_docs(docs, cp)
     total = int(sum(docs))
-    pad = (-total) % (64 * cp)             # whole 64-token tiles per rank; padding is its own document
-    docs = list(docs) + ([pad] if pad else [])
-    total += pad
     cu = torch.tensor(np.concatenate([[0], np.cumsum(docs)]).astype(np.int32), device="cuda")
     pos = sharding.shard_positions(total, cp, "contiguous")
     g = torch.Generator(device="cuda").manual_seed(seed)
@@ -272,30 +327,51 @@ def time_micro_batch(docs: Sequence[int], cp: int, hq: int = 32, hkv: int = 8, d
     dq = [torch.zeros(x.shape, device="cuda") for x in q]
     dk = [torch.zeros(x.shape, device="cuda") for x in k]
     dv = [torch.zeros(x.shape, device="cuda") for x in k]
-    ws = torch.empty(ra.ringattn_run_workspace_size(q[0], k[0], cp, cp, pass_=ra.RA_PASS_BWD,
-                                                    mask_mode=ra.RA_MASK_DOC_CAUSAL), dtype=torch.uint8,
-                     device="cuda")
+    ws = torch.empty(max(ra.ringattn_run_workspace_size(q[0], k[0], cp, 1, pass_=p_, mask_mode=ra.RA_MASK_DOC_CAUSAL)
+                         for p_ in (ra.RA_PASS_FWD, ra.RA_PASS_BWD)), dtype=torch.uint8, device="cuda")
     side = torch.cuda.Stream()
 
-    def step():
-        ra.ringattn_run(q, k, v, qp, qp, o_acc=o_acc, lse=lse, out=out, q_doc=doc, kv_doc=doc,
-                        mask_mode=ra.RA_MASK_DOC_CAUSAL, workspace=ws, copy_stream=side)
-        ra.ringattn_run(q, k, v, qp, qp, lse=lse, out=out, d_o=do, q_doc=doc, kv_doc=doc, delta=delta, dq=dq,
-                        dk=dk, dv=dv, mask_mode=ra.RA_MASK_DOC_CAUSAL, pass_=ra.RA_PASS_BWD, workspace=ws,
-                        copy_stream=side)
-    step()
+    def events(n):
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+        for e in ev:
+            e.record()   # creates the underlying event
+        return ev
+
+    def run_rank(r, ev_f, ev_b, call):
+        one = dict(q_doc=[doc[r]], kv_doc=doc, first_rank=r, mask_mode=ra.RA_MASK_DOC_CAUSAL, workspace=ws,
+                   copy_stream=side)
+        call[0].record()
+        ra.ringattn_run([q[r]], k, v, [qp[r]], qp, o_acc=[o_acc[r]], lse=[lse[r]], out=[out[r]],
+                        step_events=[e.cuda_event for e in ev_f], **one)
+        call[1].record()
+        ra.ringattn_run([q[r]], k, v, [qp[r]], qp, lse=[lse[r]], out=[out[r]], d_o=[do[r]], delta=[delta[r]],
+                        dq=[dq[r]], dk=dk, dv=dv, pass_=ra.RA_PASS_BWD, step_events=[e.cuda_event for e in ev_b],
+                        **one)
+        call[2].record()
+
+    sets = [[(events(2 * cp), events(2 * cp), events(3)) for _ in range(cp)] for _ in range(reps + 1)]
+    for rep in range(reps + 1):   # the first round is a warm-up
+        for r in range(cp):
+            run_rank(r, *sets[rep][r])
     torch.cuda.synchronize()
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
-    ev[0].record()
-    for r in range(reps):
-        step()
-        ev[r + 1].record()
-    torch.cuda.synchronize()
-    return float(np.median([ev[r].elapsed_time(ev[r + 1]) for r in range(reps)])) / cp
+    # [reps, cp ranks, cp steps] step times and [reps, cp] time outside the steps, per pass
+    step = np.zeros((2, reps, cp, cp))
+    rest = np.zeros((2, reps, cp))
+    for rep in range(reps):
+        for r in range(cp):
+            ev_f, ev_b, call = sets[rep + 1][r]
+            for pss, ev in ((0, ev_f), (1, ev_b)):
+                step[pss, rep, r] = [ev[2 * t].elapsed_time(ev[2 * t + 1]) for t in range(cp)]
+                rest[pss, rep, r] = call[pss].elapsed_time(call[pss + 1]) - step[pss, rep, r].sum()
+    med_step, med_rest = np.median(step, axis=1), np.median(rest, axis=1)   # [2, cp, cp], [2, cp]
+    ring = float(sum(med_step[p_].max(axis=0).sum() + med_rest[p_].max() for p_ in range(2)))
+    per_rank = [float(med_step[:, r].sum() + med_rest[:, r].sum()) for r in range(cp)]
+    return RingTiming(ring, per_rank)
 
 
-def measure(grid_tokens=(8192, 16384, 32768), doc_lengths=(512, 2048, 8192, 32768), cps=(1, 2, 4, 8)):
-    """Timings for the cost-model fit: micro-batches of equal documents, every CP size."""
+def measure(grid_tokens=(8192, 16384, 32768), doc_lengths=(512, 2048, 8192, 32768), cps=(1, 2, 4, 8), **timing):
+    """Timings for the cost-model fit: micro-batches of equal documents, every CP size
+    (`timing`: head counts, head_dim, reps of `time_micro_batch`)."""
     samples = []
     for tot in grid_tokens:
         for dl in doc_lengths:
@@ -303,18 +379,19 @@ def measure(grid_tokens=(8192, 16384, 32768), doc_lengths=(512, 2048, 8192, 3276
                 continue
             docs = [dl] * (tot // dl)
             for c in cps:
-                if tot // c < 64:
+                if tot // c < TILE:
                     continue
-                samples.append((docs, c, time_micro_batch(docs, c)))
+                samples.append((docs, c, time_micro_batch(docs, c, **timing).ms))
     return samples
 
 
-def execute(plan: Plan, lengths: Sequence[int], n_gpus: int) -> float:
+def execute(plan: Plan, lengths: Sequence[int], n_gpus: int, **timing) -> float:
     """Measured iteration time of a plan: every micro-batch is timed on this GPU at its CP
-    size (`time_micro_batch`) and charged to the GPUs of its group."""
+    size (`time_micro_batch`: the ring's slowest-rank critical path) and charged to the
+    GPUs of its group."""
     loads = [0.0] * n_gpus
     for mb in plan.micro_batches:
-        t = time_micro_batch([lengths[i] for i in mb.seqs], mb.cp)
+        t = time_micro_batch([lengths[i] for i in mb.seqs], mb.cp, **timing).ms
         for g in range(mb.group * mb.cp, (mb.group + 1) * mb.cp):
             loads[g] += t
     return max(loads)
@@ -332,6 +409,7 @@ def main(argv=None):
     args = ap.parse_args(argv)
     samples = measure()
     model, err = fit_cost_model(samples)
+    mean_err = float(np.mean([abs(model.predict(d, c) - ms) / ms for d, c, ms in samples]))
     lengths = lognormal_lengths(args.seed, args.sequences)
     dyn = solve_dynamic(lengths, args.gpus, args.tokens_per_gpu, model)
     sta = solve_static(lengths, args.gpus, args.tokens_per_gpu, model)
@@ -339,7 +417,9 @@ def main(argv=None):
         check_plan(p, lengths, args.gpus, args.tokens_per_gpu)
     t_dyn, t_sta = execute(dyn, lengths, args.gpus), execute(sta, lengths, args.gpus)
     print(json.dumps({
+        "timing": "per micro-batch: sum over ring steps of the slowest rank's step time, forward + backward",
         "cost_model": dataclasses.asdict(model), "fit_samples": len(samples), "fit_max_rel_err": round(err, 4),
+        "fit_mean_rel_err": round(mean_err, 4),
         "worst_fit": sorted(([len(d), d[0], c, round(ms, 3), round(model.predict(d, c), 3)] for d, c, ms in samples),
                             key=lambda r: -abs(r[4] - r[3]) / r[3])[:6],
         "batch": {"sequences": len(lengths), "tokens": int(sum(lengths)), "longest": max(lengths),

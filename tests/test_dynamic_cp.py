@@ -1,17 +1,59 @@
 """Dynamic-CP cost model and solver (host): fit, plan constraints, and the heuristic against
 the exhaustive optimum of oracle/dynamic_cp.py on small instances."""
+from functools import lru_cache
+
 import numpy as np
 import pytest
 
 from oracle.dynamic_cp import optimal_time
 from ring_attention_ringattn_amd import dynamic_cp as dcp
 
-MODEL = dcp.CostModel(alpha=2e-8, beta=1e-4, eps=2e-6, gamma=0.05, delta=0.1)
+MODEL = dcp.CostModel(alpha=4e-8, beta=1e-4, eps=2e-6, gamma=0.05, delta=0.1)
+
+
+@lru_cache(maxsize=None)
+def _critical(docs, c):
+    """Pairs on the ring's critical path, counted query token by query token: the packed
+    stream padded to whole 64-token tiles per rank (the padding its own document), split
+    contiguously; at step t rank r holds block (r - t) mod c; a query sees the keys of its
+    own document at or before it; each step counts its busiest rank."""
+    pad = (-sum(docs)) % (64 * c)
+    lens = list(docs) + ([pad] if pad else [])
+    n = sum(lens)
+    s = n // c
+    doc_start = np.repeat(np.cumsum([0] + lens[:-1]), lens)
+    total = 0
+    for t in range(c):
+        busiest = 0
+        for r in range(c):
+            j = (r - t) % c
+            qpos = np.arange(r * s, (r + 1) * s)
+            first = np.maximum(doc_start[qpos], j * s)
+            last = np.minimum(qpos, (j + 1) * s - 1)
+            busiest = max(busiest, int(np.maximum(last - first + 1, 0).sum()))
+        total += busiest
+    return total
 
 
 def _cost(docs, c):
     # the same cost form, written out independently for the oracle
-    return (2e-8 * sum(x * x for x in docs) + 1e-4 * sum(docs)) / c + 2e-6 * sum(docs) + 0.05 * c + 0.1
+    n = sum(docs)
+    return 4e-8 * _critical(tuple(docs), c) + 1e-4 * n / c + 2e-6 * n + 0.05 * c + 0.1
+
+
+def test_step_pairs_against_a_token_by_token_count():
+    rng = np.random.default_rng(11)
+    for _ in range(40):
+        docs = [int(x) for x in rng.integers(1, 900, rng.integers(1, 7))]
+        c = int(rng.choice([1, 2, 4, 8]))
+        assert dcp.critical_pairs(docs, c) == _critical(tuple(docs), c), (docs, c)
+    # one document over c ranks: P_crit is the last rank's work, (2c - 1) / c times the mean
+    d = 64 * 8 * 16
+    assert dcp.critical_pairs([d], 8) == (d // 8) ** 2 * 7 + (d // 8) * (d // 8 + 1) // 2
+    # every rank's pairs over the ring add up to the micro-batch's pairs
+    docs = [700, 1300, 250]
+    per = dcp.step_pairs(docs, 4)
+    assert per.sum() == sum(x * (x + 1) // 2 for x in dcp.ring_docs(docs, 4))
 
 
 def test_fit_recovers_a_known_model():
