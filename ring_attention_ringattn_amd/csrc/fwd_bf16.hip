@@ -97,7 +97,8 @@ __device__ __forceinline__ void map_block(int n_qt, int hq, int hkv, int total, 
 }  // namespace
 
 // MULTI: several resident blocks (entries carry a block index); otherwise block 0 only.
-template <int D, bool MULTI>
+// KREL: byte offsets of K rows within a block fit 31 bits (one resource per block).
+template <int D, bool MULTI, bool KREL>
 __global__ __launch_bounds__(NWAVES * 64, 1) void fwd_bf16_kernel(FwdArgs a) {
   using C = Cfg<D>;
   __shared__ __attribute__((aligned(1024))) __bf16 Ks[NBUF][BN * D];
@@ -170,14 +171,19 @@ __global__ __launch_bounds__(NWAVES * 64, 1) void fwd_bf16_kernel(FwdArgs a) {
     vtoff_lane[c] = r * skp * 2 + (((p & 7) ^ vswz(r)) << 4);
   }
 
-  // Block pointers of the tiles being issued.  One block: loop invariant.  Several:
-  // the list runs through the blocks in order, so each side (K, V) keeps the
-  // pointers of its current block and reloads them only when the block changes
-  // (a reload is a scalar memory load the issue must wait for).
-  const __bf16* kblk_p = (const __bf16*)a.kb[0];
-  const int* kpos_p = a.kposb[0];
-  const int* kdoc_p = a.kdocb[0];
-  const __bf16* vblk_p = (const __bf16*)a.vtb[0];
+  // Buffer resources of the block being issued, built once per block: the K rows of this
+  // (batch, kv head), its V^T rows, the key positions and documents.  A tile is then issued
+  // with its byte offset added to each lane's offset, and the range check zero-fills keys
+  // past the block's end.  KREL: the K offsets fit 31 bits (else, very wide token-major
+  // blocks, each K tile gets a resource of its own).  One block: loop invariant.  Several:
+  // the list runs through the blocks in order, so each side (K, V) rebuilds its resources
+  // only when the block changes.
+  const int kspan = KREL ? a.sk * rsb : 0, pspan = a.sk * 4, vspan = D * skp * 2;
+  const __bf16* kblk_p = (const __bf16*)a.kb[0] + kvoff;
+  i32x4 k_rsrc = buffer_rsrc(kblk_p, kspan);
+  i32x4 kpos_rsrc = buffer_rsrc(a.kposb[0], pspan);
+  i32x4 kdoc_rsrc = buffer_rsrc(mask == MASK_DOC_CAUSAL ? a.kdocb[0] : a.kposb[0], pspan);
+  i32x4 v_rsrc = buffer_rsrc((const __bf16*)a.vtb[0] + vtoff, vspan);
   int kblk = 0, vblk = 0;
 
   // Start streaming the K rows (with the key positions and documents, wave 0)
@@ -190,21 +196,28 @@ __global__ __launch_bounds__(NWAVES * 64, 1) void fwd_bf16_kernel(FwdArgs a) {
       const int blk = (ent >> 12) & 0xf;
       if (blk != kblk) {
         kblk = blk;
-        kblk_p = (const __bf16*)a.kb[blk];
-        kpos_p = a.kposb[blk];
-        kdoc_p = a.kdocb[blk];
+        kblk_p = (const __bf16*)a.kb[blk] + kvoff;
+        if (KREL) k_rsrc = buffer_rsrc(kblk_p, kspan);
+        kpos_rsrc = buffer_rsrc(a.kposb[blk], pspan);
+        if (mask == MASK_DOC_CAUSAL) kdoc_rsrc = buffer_rsrc(a.kdocb[blk], pspan);
       }
     }
     const int kbase = tile * BN;
-    const int rows = min(BN, a.sk - kbase);
     if (wave == 0) {
-      dma4(kpos_p + kbase, rows * 4, (RA_LDS void*)&kvp[buf][0], lane * 4);
-      if (mask == MASK_DOC_CAUSAL) dma4(kdoc_p + kbase, rows * 4, (RA_LDS void*)&kvd[buf][0], lane * 4);
+      dma4r(kpos_rsrc, (RA_LDS void*)&kvp[buf][0], (kbase + lane) * 4);
+      if (mask == MASK_DOC_CAUSAL) dma4r(kdoc_rsrc, (RA_LDS void*)&kvd[buf][0], (kbase + lane) * 4);
     }
-    const __bf16* kb = kblk_p + kvoff + (size_t)kbase * a.kvs.s;
+    if (KREL) {
+      const int ko = kbase * rsb;
 #pragma unroll
-    for (int c = 0; c < C::CPW; ++c)
-      dma16(kb, rows * rsb, (RA_LDS void*)&Ks[buf][(c * NWAVES + wave) * 512], voff[c]);
+      for (int c = 0; c < C::CPW; ++c) dma16r(k_rsrc, (RA_LDS void*)&Ks[buf][(c * NWAVES + wave) * 512], voff[c] + ko);
+    } else {
+      const int rows = min(BN, a.sk - kbase);
+      const __bf16* kb = kblk_p + (size_t)kbase * a.kvs.s;
+#pragma unroll
+      for (int c = 0; c < C::CPW; ++c)
+        dma16(kb, rows * rsb, (RA_LDS void*)&Ks[buf][(c * NWAVES + wave) * 512], voff[c]);
+    }
   };
   // V^T rows of the tile: D rows of 64 keys (the padding past the block end is zero)
   auto issue_v = [&] __device__(int li, int ent) {
@@ -213,14 +226,13 @@ __global__ __launch_bounds__(NWAVES * 64, 1) void fwd_bf16_kernel(FwdArgs a) {
       const int blk = (ent >> 12) & 0xf;
       if (blk != vblk) {
         vblk = blk;
-        vblk_p = (const __bf16*)a.vtb[blk];
+        v_rsrc = buffer_rsrc((const __bf16*)a.vtb[blk] + vtoff, vspan);
       }
     }
-    const int kbase = tile * BN;
-    const __bf16* vb = vblk_p + vtoff + kbase;
+    const int vo = tile * BN * 2;
 #pragma unroll
     for (int c = 0; c < C::CPW; ++c)
-      dma16(vb, (D * skp - kbase) * 2, (RA_LDS void*)&Vs[buf][(c * NWAVES + wave) * 512], vtoff_lane[c]);
+      dma16r(v_rsrc, (RA_LDS void*)&Vs[buf][(c * NWAVES + wave) * 512], vtoff_lane[c] + vo);
   };
 
   // V^T operands (lane j: head dimension db*32 + j, 8 keys) of the transposed tile in V
@@ -364,11 +376,12 @@ __global__ __launch_bounds__(NWAVES * 64, 1) void fwd_bf16_kernel(FwdArgs a) {
       }
       q_loaded = true;
     }
-    auto tile_of = [&] __device__(int li) { return __builtin_amdgcn_readfirstlane(list[li]) & 0xffff; };
+    // list entry li (tile | block << 12 | class << 24), scalar
+    auto tile_of = [&] __device__(int li) { return __builtin_amdgcn_readfirstlane(list[li]); };
 
     // prologue: K(0..2), V(0..1); V(-1) := 0 and P := 0 so that period 0's PV adds nothing
-    for (int t = 0; t < min(3, total); ++t) issue_k(t, tile_of(t));
-    for (int t = 0; t < min(2, total); ++t) issue_v(t, tile_of(t));
+    for (int t = 0; t < min(3, total); ++t) issue_k(t, tile_of(t) & 0xffff);
+    for (int t = 0; t < min(2, total); ++t) issue_v(t, tile_of(t) & 0xffff);
     for (int e = tid * 8; e < BN * D; e += NWAVES * 64 * 8) *(bf16x8*)&Vs[NBUF - 1][e] = bf16x8{};
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) pf[kk] = bf16x8{};
@@ -391,33 +404,64 @@ __global__ __launch_bounds__(NWAVES * 64, 1) void fwd_bf16_kernel(FwdArgs a) {
     // its softmax phase of period i+1.  Leading loads thus have about two
     // periods to land, trailing ones one and a half, and the waits sit where
     // the loads are normally long done.
+    //
+    // The periods that issue both tiles (all but the last three) run in a loop
+    // with no conditions; the last ones drain.  List entries (workgroup-uniform)
+    // rotate through scalar registers: period i reads the entry of tile i+4
+    // from LDS and turns it scalar one period later, when it has long arrived.
+    int ent0 = tile_of(0), ent1 = tile_of(min(1, LIST - 1)), ent2 = tile_of(min(2, LIST - 1));
+    int nxt = list[min(3, LIST - 1)];
     if (!leading) __syncthreads();
-    for (int i = 0; i <= total; ++i) {
+    int i = 0;
+    // (phase_barrier: the matrix work must not drift past the barrier into the softmax
+    // phase, nor the softmax work into the matrix phase: MFMAs touch no memory, so the
+    // workgroup barrier alone does not hold them)
+    auto phase_barrier = [] __device__() {
+      __builtin_amdgcn_sched_barrier(0);
+      __syncthreads();
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    for (; i + 3 < total; ++i) {
       matrix((i + NBUF - 1) % NBUF, i % NBUF, pf, s);
-      // This wave's loads of period i-2 have landed (those of period i-1 may still
-      // be in flight): vmcnt = what period i-1 issued, 2 CPW for K and V, CPW for V
-      // alone (wave 0's position loads only make the wait stricter).
+      wait_vmem_n<2 * C::CPW>();   // period i-1 issued K(i+2) and V(i+1); period i-2's loads have landed
+      phase_barrier();
+      const int ent3 = __builtin_amdgcn_readfirstlane(nxt);
+      nxt = list[min(i + 4, LIST - 1)];
+      issue_k(i + 3, ent3 & 0xffff);
+      issue_v(i + 2, ent2 & 0xffff);
+      prefetch_v(i % NBUF);   // V(i), read by the next period's PV
+      softmax(ent0, i % NBUF, s, pf);
+      // The leading group's softmax(i+1), which starts at the next barrier, reads V(i+1)
+      // early (prefetch_v), and a quarter of that tile arrives through the trailing
+      // waves' loads of period i-1: the trailing group waits for them here (what
+      // period i issued after them, K(i+3) and V(i+2), may still be in flight).
+      if (!leading) wait_vmem_n<2 * C::CPW>();
+      phase_barrier();
+      ent0 = ent1;
+      ent1 = ent2;
+      ent2 = ent3;
+    }
+    for (; i <= total; ++i) {
+      matrix((i + NBUF - 1) % NBUF, i % NBUF, pf, s);
+      // this wave's loads of period i-2 have landed: vmcnt = what period i-1 issued
+      // (K(i+2) if it exists, V(i+1) if it exists; wave 0's position loads only make
+      // the wait stricter)
       if (i + 2 < total) wait_vmem_n<2 * C::CPW>();
       else if (i + 1 < total) wait_vmem_n<C::CPW>();
       else wait_vmem();
-      __syncthreads();
-      const int e0 = list[min(i, LIST - 1)], e2 = list[min(i + 2, LIST - 1)], e3 = list[min(i + 3, LIST - 1)];
-      // list entries are workgroup-uniform: keep them scalar so the branches on them stay branches
-      if (i + 3 < total) issue_k(i + 3, __builtin_amdgcn_readfirstlane(e3) & 0xffff);
-      if (i + 2 < total) issue_v(i + 2, __builtin_amdgcn_readfirstlane(e2) & 0xffff);
-      if (i < total) prefetch_v(i % NBUF);   // V(i), read by the next period's PV
-      if (i < total) softmax(__builtin_amdgcn_readfirstlane(e0), i % NBUF, s, pf);
-      // The leading group's softmax(i+1), which starts at the next barrier, reads V(i+1)
-      // early (prefetch_v), and a quarter of that tile arrives through the trailing
-      // waves' loads of period i-1.  So the trailing group waits for those loads here,
-      // one phase earlier than its own reads need: vmcnt = what period i issued after
-      // them (K(i+3) and V(i+2), each only if it exists).
-      if (!leading && i + 1 < total) {
-        if (i + 3 < total) wait_vmem_n<2 * C::CPW>();
-        else if (i + 2 < total) wait_vmem_n<C::CPW>();
+      phase_barrier();
+      if (i + 2 < total) issue_v(i + 2, ent2 & 0xffff);
+      if (i < total) {
+        prefetch_v(i % NBUF);
+        softmax(ent0, i % NBUF, s, pf);
+      }
+      if (!leading && i + 1 < total) {   // as above; period i issued at most V(i+2)
+        if (i + 2 < total) wait_vmem_n<C::CPW>();
         else wait_vmem();
       }
-      __syncthreads();
+      phase_barrier();
+      ent0 = ent1;
+      ent1 = ent2;
     }
     if (leading) __syncthreads();
   }
@@ -466,10 +510,18 @@ hipError_t launch_fwd_bf16(const FwdArgs& a, int d, hipStream_t st) {
   const long blocks = (long)((a.sq + BM - 1) / BM) * a.hq * a.B;
   if (blocks == 0) return hipSuccess;
   const bool multi = a.n_blocks > 1;
-  if (d == 128 && multi) fwd_bf16_kernel<128, true><<<(unsigned)blocks, NWAVES * 64, 0, st>>>(a);
-  else if (d == 128) fwd_bf16_kernel<128, false><<<(unsigned)blocks, NWAVES * 64, 0, st>>>(a);
-  else if (multi) fwd_bf16_kernel<64, true><<<(unsigned)blocks, NWAVES * 64, 0, st>>>(a);
-  else fwd_bf16_kernel<64, false><<<(unsigned)blocks, NWAVES * 64, 0, st>>>(a);
+  // the largest K offset of a tile load is below (tiles * 64) rows of the block
+  const bool krel = (int64_t)n_tiles(a.sk) * TILE * a.kvs.s * 2 < ((int64_t)1 << 31);
+  const dim3 grid((unsigned)blocks), block(NWAVES * 64);
+#define RA_FWD_LAUNCH(DD, MM, KK) fwd_bf16_kernel<DD, MM, KK><<<grid, block, 0, st>>>(a)
+  if (d == 128) {
+    if (multi) { if (krel) RA_FWD_LAUNCH(128, true, true); else RA_FWD_LAUNCH(128, true, false); }
+    else { if (krel) RA_FWD_LAUNCH(128, false, true); else RA_FWD_LAUNCH(128, false, false); }
+  } else {
+    if (multi) { if (krel) RA_FWD_LAUNCH(64, true, true); else RA_FWD_LAUNCH(64, true, false); }
+    else { if (krel) RA_FWD_LAUNCH(64, false, true); else RA_FWD_LAUNCH(64, false, false); }
+  }
+#undef RA_FWD_LAUNCH
   return hipGetLastError();
 }
 

@@ -97,6 +97,19 @@ __device__ __forceinline__ void dma4(const void* base, int nbytes, RA_LDS void* 
                :: "v"(voff), "s"(buffer_rsrc(base, nbytes)), "{m0}"(lds_addr(dst)) : "memory");
 }
 
+// The same with a resource built once (buffer_rsrc over a whole block) and each lane's
+// byte offset within it: the range check then zero-fills everything at or past the
+// block's end, and issuing a tile costs no descriptor arithmetic.
+__device__ __forceinline__ void dma16r(i32x4 rsrc, RA_LDS void* dst, int voff) {
+  asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+               :: "v"(voff), "s"(rsrc), "{m0}"(lds_addr(dst)) : "memory");
+}
+
+__device__ __forceinline__ void dma4r(i32x4 rsrc, RA_LDS void* dst, int voff) {
+  asm volatile("s_nop 0\n\tbuffer_load_dword %0, %1, 0 offen lds"
+               :: "v"(voff), "s"(rsrc), "{m0}"(lds_addr(dst)) : "memory");
+}
+
 __device__ __forceinline__ s16x4 lds_read_tr16(const __bf16* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((RA_LDS s16x4*)p);
 }
