@@ -486,6 +486,91 @@ def summarize_trace(trace_dir, bench_log):
     return "\n".join(head + out) + "\n\nThe bench line of this run:\n\n    " + line + "\n"
 
 
+def _counter_rows(path):
+    """Per dispatch of a rocprofv3 counter run: (kernel, grid, block, dispatch) -> ({counter: value}, ns)."""
+    import csv
+    rows, dur = {}, {}
+    for r in csv.DictReader(open(path)):
+        key = (_demangle(r["Kernel_Name"]), int(r["Grid_Size"]), int(r["Workgroup_Size"]), int(r["Dispatch_Id"]))
+        rows.setdefault(key, {})
+        rows[key][r["Counter_Name"]] = rows[key].get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+        dur[key] = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+    return rows, dur
+
+
+def summarize_counters(run_dirs, cal_dirs, traffic_out=None):
+    """Markdown table of the ring library's kernels from rocprofv3 counter runs of this script
+    (each run a directory holding *counter_collection.csv; counters of several runs are joined
+    per kernel and launch shape).  HBM bytes are FETCH_SIZE and WRITE_SIZE scaled by what the
+    same counters read for a plain device copy of known size (`--copy-calibration`, cal_dirs:
+    the FETCH_SIZE and the WRITE_SIZE run).  With traffic_out, the forward step kernel's HBM bytes
+    per launch are written there for the bench line's roofline."""
+    import glob
+    find = lambda d: glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)[0]
+    copy_bytes = 64 * 1024 * 1024 * 4
+    cal = {}
+    for d in cal_dirs:
+        rows, _ = _counter_rows(find(d))
+        for (k, g, b, _), c in rows.items():
+            if k.startswith("__amd_rocclr_copyBuffer") or "copy" in k.lower():
+                for n, v in c.items():
+                    cal.setdefault(n, []).append(v)
+    # the copies: the largest readings are the 256 MiB copies (the fill before them is smaller)
+    fetch_kib = sorted(cal.get("FETCH_SIZE", [0.0]))[-1]
+    write_kib = sorted(cal.get("WRITE_SIZE", [0.0]))[-1]
+    fscale = copy_bytes / (fetch_kib * 1024) if fetch_kib else float("nan")
+    wscale = copy_bytes / (write_kib * 1024) if write_kib else float("nan")
+    agg = {}
+    for d in run_dirs:
+        rows, dur = _counter_rows(find(d))
+        for key, c in rows.items():
+            k, g, b, _ = key
+            if not k.startswith("ra::"):
+                continue
+            a = agg.setdefault((k, g, b), {"n": {}, "c": {}, "ns": []})
+            a["ns"].append(dur[key])
+            for n, v in c.items():
+                a["c"][n] = a["c"].get(n, 0.0) + v
+                a["n"][n] = a["n"].get(n, 0) + 1
+    out = ["| kernel | grid (threads) | block | avg us | clock GHz | MFMA busy % | executed TFLOP/s | LDS bank "
+           "conflicts | HBM read GB | HBM write GB | HBM TB/s |", "|---|---|---|---|---|---|---|---|---|---|---|"]
+    per = {}
+    for (k, g, b), a in sorted(agg.items(), key=lambda kv: -sum(kv[1]["ns"])):
+        m = {n: a["c"][n] / a["n"][n] for n in a["c"]}
+        ns = sum(a["ns"]) / len(a["ns"])
+        gui = m.get("GRBM_GUI_ACTIVE")
+        clk = gui / 8 / ns if gui else float("nan")
+        busy = 100 * m["SQ_VALU_MFMA_BUSY_CYCLES"] / (gui / 8 * 1024) if gui and "SQ_VALU_MFMA_BUSY_CYCLES" in m else float("nan")
+        tf = m.get("SQ_INSTS_VALU_MFMA_MOPS_BF16", float("nan")) * 512 / ns / 1e3
+        rd = m.get("FETCH_SIZE", float("nan")) * 1024 * fscale
+        wr = m.get("WRITE_SIZE", float("nan")) * 1024 * wscale
+        per[(k, g, b)] = (rd, wr)
+        out.append(f"| `{k}` | {g} | {b} | {ns / 1e3:.1f} | {clk:.2f} | {busy:.1f} | {tf:.0f} | "
+                   f"{m.get('SQ_LDS_BANK_CONFLICT', float('nan')):.0f} | {rd / 1e9:.3f} | {wr / 1e9:.3f} | "
+                   f"{(rd + wr) / ns / 1e3:.2f} |")
+    head = (f"Copy calibration: a 256 MiB device copy reads FETCH_SIZE {fetch_kib:.1f} KiB and WRITE_SIZE "
+            f"{write_kib:.1f} KiB, so HBM read = FETCH_SIZE x {fscale:.3f}, write = WRITE_SIZE x {wscale:.3f}. "
+            "Clock = GRBM_GUI_ACTIVE / 8 XCDs / launch duration; MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / "
+            "(GRBM_GUI_ACTIVE / 8 x 1024 SIMDs); executed TFLOP/s = SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512 / duration "
+            "(masked parts of partial tiles included). Averages per launch over the launches of each kernel "
+            "and launch shape; durations are those of the counter runs (dispatches serialised).\n\n")
+    if traffic_out:
+        fwd = [(kgb, v) for kgb, v in per.items() if kgb[0].startswith("ra::fwd_bf16_kernel<128, false")]
+        (kgb, (rd, wr)), = [max(fwd, key=lambda x: x[0][1])]
+        json.dump({"kernel": kgb[0], "grid_threads": kgb[1],
+                   "workload": "131072-token rank share, one ring step (16384 queries x 16384 keys, 32/8 heads, "
+                               "D = 128): every launch of the headline ring",
+                   "kernel_source_sha256": kernel_source_hash(),
+                   "copy_calibration": {"bytes_read_and_written_per_copy": copy_bytes, "fetch_kib_raw": fetch_kib,
+                                        "write_kib_raw": write_kib, "fetch_scale": fscale, "write_scale": wscale},
+                   "hbm_fetch_bytes_per_launch": rd, "hbm_write_bytes_per_launch": wr,
+                   "hbm_bytes_per_launch": rd + wr,
+                   "algorithmic_bytes_per_launch": {"q_bytes": 134217728, "kv_bytes": 67108864,
+                                                    "o_acc_read_write": 536870912, "lse_read_write": 4194304},
+                   "algorithmic_total": 742391808}, open(traffic_out, "w"), indent=1)
+    return head + "\n".join(out) + "\n"
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -503,9 +588,18 @@ def main():
                     help="only run a plain 256 MiB device copy (for scaling HBM byte counters)")
     ap.add_argument("--summarize-trace", nargs=2, metavar=("TRACE_DIR", "BENCH_LOG"),
                     help="print the markdown summary of a rocprofv3 trace of this script and exit (no GPU)")
+    ap.add_argument("--summarize-counters", nargs="+", metavar="RUN_DIR",
+                    help="print the markdown table of rocprofv3 counter runs of this script and exit (no GPU); "
+                         "needs --calibration")
+    ap.add_argument("--calibration", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="counter runs of --copy-calibration (FETCH_SIZE, then WRITE_SIZE)")
+    ap.add_argument("--traffic-out", help="with --summarize-counters: write the forward step's HBM bytes here")
     args = ap.parse_args()
     if args.summarize_trace:
         print(summarize_trace(*args.summarize_trace), end="")
+        return
+    if args.summarize_counters:
+        print(summarize_counters(args.summarize_counters, args.calibration, args.traffic_out), end="")
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU's share of the ring; --gpus {args.gpus} is not supported "
