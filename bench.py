@@ -457,7 +457,7 @@ def summarize_trace(trace_dir, bench_log):
                 return n
         return "c3_ring" if ranges else "-"
     agg = {}
-    step = []
+    step, step_name = [], None
     for r in rows:
         n = _demangle(r["Kernel_Name"])
         if not (n.startswith("ra::") or n.startswith("__amd_rocclr_copyBuffer")):
@@ -465,8 +465,9 @@ def summarize_trace(trace_dir, bench_log):
         leg = leg_of(int(r["Start_Timestamp"]))
         dur = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
         agg.setdefault((leg, n, int(r["Grid_Size_X"]), int(r["Workgroup_Size_X"])), []).append(dur)
-        if leg in ("c3_ring", "-") and n.startswith("ra::fwd_bf16_kernel<128, false>"):
+        if leg in ("c3_ring", "-") and n.startswith("ra::fwd_bf16_kernel<128, false"):
             step.append(dur)
+            step_name = n
     out = ["| leg | kernel | grid (threads) | block | launches | avg us | min us | max us |",
            "|---|---|---|---|---|---|---|---|"]
     for (leg, n, g, b), d in sorted(agg.items(), key=lambda kv: (kv[0][0], -sum(kv[1]))):
@@ -477,7 +478,7 @@ def summarize_trace(trace_dir, bench_log):
     tf = sum(flops) * k / (sum(timed_steps) / 1e6) / 1e12 if timed_steps else float("nan")
     per_step = [sum(timed_steps[t::nsteps]) / k for t in range(nsteps)] if timed_steps else []
     head = [
-        f"Headline forward step kernel `ra::fwd_bf16_kernel<128, false>`, the {k} timed rings ({k * nsteps} "
+        f"Headline forward step kernel `{step_name}`, the {k} timed rings ({k * nsteps} "
         f"launches, after {bench['warmup']} warm-up rings): average {sum(timed_steps) / len(timed_steps):.1f} us per "
         f"launch; per ring step (us) {[round(x, 1) for x in per_step]}; {tf:.1f} TFLOP/s over the causal-effective "
         f"FLOPs of those launches, frac {tf / PEAK_BF16_TFLOPS:.4f} of {PEAK_BF16_TFLOPS} (the bench line of the same "
