@@ -320,7 +320,8 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void bwd_dq_kernel(BwdArg
   __shared__ int list[LISTN];
   __shared__ int wave_cnt[NW];
 
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, g = lane >> 5, j = lane & 31;
+  const int tid = threadIdx.x, lane = tid & 63, g = lane >> 5, j = lane & 31;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: the head and row bases stay scalar
   const int n_qt = (a.sq + BMQ - 1) / BMQ;
   const int grp = a.hq / a.hkv;
   int r = xcd_logical(blockIdx.x, n_qt * (a.hq / HPW) * a.B);
@@ -341,7 +342,6 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void bwd_dq_kernel(BwdArg
   // this wave's 32 query rows: Q and dO as MFMA B operands (lane j = row)
   const int qrow = q0 + (wave & 3) * 32 + j;
   const bool qvalid = qrow < a.sq;
-  const size_t qoff = b * a.qs.b + h * a.qs.h + (size_t)qrow * a.qs.s;
   // (loaded once the first tile list with a visible tile exists)
   bf16x8 qf[D / 16], of[D / 16];
   bool q_loaded = false;
@@ -403,11 +403,15 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void bwd_dq_kernel(BwdArg
     seen += total;
     if (total == 0) continue;
     if (!q_loaded) {
+      // the row's address is formed here, not held across the loop (registers are scarce)
+      int qr_ = qrow, g_ = g;
+      asm volatile("" : "+v"(qr_), "+v"(g_));
+      const size_t qoff = b * a.qs.b + h * a.qs.h + (size_t)qr_ * a.qs.s + g_ * 8;
 #pragma unroll
       for (int ks = 0; ks < D / 16; ++ks) {
         bf16x8 z = {};
-        qf[ks] = qvalid ? *(const bf16x8*)((const __bf16*)a.q + qoff + ks * 16 + g * 8) : z;
-        of[ks] = qvalid ? *(const bf16x8*)((const __bf16*)a.d_o + qoff + ks * 16 + g * 8) : z;
+        qf[ks] = qvalid ? *(const bf16x8*)((const __bf16*)a.q + qoff + ks * 16) : z;
+        of[ks] = qvalid ? *(const bf16x8*)((const __bf16*)a.d_o + qoff + ks * 16) : z;
       }
       q_loaded = true;
     }
@@ -473,14 +477,17 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void bwd_dq_kernel(BwdArg
     }
   }
 
-  if (!qvalid || seen == 0) return;   // seen == 0: nothing visible, dq stays as it is
+  // this lane's row again, from the lane id (not held across the loop: registers are scarce)
+  const int ln_ = __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+  const int qr_ = q0 + (wave & 3) * 32 + (ln_ & 31);
+  if (qr_ >= a.sq || seen == 0) return;   // seen == 0: nothing visible, dq stays as it is
   // dq += scale dQ; C layout of dQ^T: lane (g, j), value v -> dim db*32 + 8*(v/4) + 4*g + v%4, query j
-  float* dqp = a.dq + lrow * D;
+  float* dqp = a.dq + (((size_t)b * a.hq + h) * a.sq + qr_) * D;
 #pragma unroll
   for (int db = 0; db < D / 32; ++db)
 #pragma unroll
     for (int vh = 0; vh < 4; ++vh) {
-      const int d = db * 32 + vh * 8 + g * 4;
+      const int d = db * 32 + vh * 8 + (ln_ >> 5) * 4;
       f32x4 o = *(const f32x4*)(dqp + d);
 #pragma unroll
       for (int e = 0; e < 4; ++e) o[e] += a.scale * dq[db][vh * 4 + e];
