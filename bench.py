@@ -232,8 +232,25 @@ def fwd_bwd_leg(name, ranks, side, steps, warmup, label):
             "fwd_bwd_pct_peak": round(100.0 * (fl_f + fl_b) / (t_f + t_b) / 1e12 / PEAK_BF16_TFLOPS, 2)}
 
 
+def captured(fn):
+    """fn (one ring: its launches on the current stream and the copy stream) captured once as a
+    HIP graph; replaying it launches the same kernels without the per-launch host work."""
+    import torch
+    fn()
+    torch.cuda.synchronize()
+    cap = torch.cuda.Stream()
+    cap.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=cap):
+        fn()
+    torch.cuda.synchronize()
+    return g
+
+
 def fwd_ring_leg(name, side, steps, warmup, label):
-    """Forward ring of every rank of a small workload (all N ranks emulated in one ringattn_run)."""
+    """Forward ring of every rank of a small workload (all N ranks emulated in one ringattn_run),
+    launched eagerly and as a replayed HIP graph of the same ring (these rings are short enough
+    for launch latency to matter)."""
     import torch
 
     import synthetic
@@ -241,11 +258,14 @@ def fwd_ring_leg(name, side, steps, warmup, label):
     s = setup_share(name, w.ranks(), with_bwd=False)
     p = sum(s["pairs_per_step"])
     t = timed(lambda: run_fwd(s, side), steps, warmup)
+    g = captured(lambda: run_fwd(s, side))
+    tg = timed(g.replay, steps, warmup)
     fl = 4.0 * w.head_dim * w.hq * w.batch * p
-    del s
+    del g, s
     torch.cuda.empty_cache()
     return {"workload": label, "visible_pairs_per_head": p, "us_per_ring": round(t * 1e6, 1),
-            "fwd_tflops": round(fl / t / 1e12, 3), "pct_peak": round(100.0 * fl / t / 1e12 / PEAK_BF16_TFLOPS, 3)}
+            "fwd_tflops": round(fl / t / 1e12, 3), "pct_peak": round(100.0 * fl / t / 1e12 / PEAK_BF16_TFLOPS, 3),
+            "us_per_ring_graph": round(tg * 1e6, 1), "fwd_tflops_graph": round(fl / tg / 1e12, 3)}
 
 
 def hbm_leg(steps, warmup):

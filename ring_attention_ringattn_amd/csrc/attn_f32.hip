@@ -1,10 +1,13 @@
 // fp32 ring-step kernels (forward and backward).
 //
 // The fp32 problems of this library are small (launch-latency bound), so
-// these kernels favour plainness: one wave per row, the head dimension spread
-// over the 64 lanes (1 or 2 elements per lane), dot products reduced across
-// the wave, and exact expf/logf.  Key tiles whose whole range the mask hides
-// are skipped with the same per-tile ranges as the bf16 kernels.
+// these kernels favour plainness: one wave per row and exact expf/logf.  The
+// forward spreads the 64 keys of a tile over the lanes for the scores (each
+// lane one key's dot product), then the head dimension over the lanes for the
+// P V product (each key's probability read from its lane); the backward kernels
+// spread the head dimension over the lanes (1 or 2 elements per lane) and reduce
+// dot products across the wave.  Key tiles whose whole range the mask hides are
+// skipped with the same per-tile ranges as the bf16 kernels.
 #include "ra_internal.h"
 
 namespace ra {
@@ -34,7 +37,13 @@ __device__ __forceinline__ void combine(float la, float lb, float& lse, float& w
 
 }  // namespace
 
-// Forward: one wave per (b, h, query row).
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
+  return x;
+}
+
+// Forward: one wave per (b, h, query row); online softmax over 64-key tiles.
 template <int D>
 __global__ __launch_bounds__(256) void fwd_f32_kernel(FwdArgs a) {
   constexpr int PER = D / 64;
@@ -46,12 +55,15 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(FwdArgs a) {
   const int h = (wid / a.sq) % a.hq;
   const int b = wid / ((long)a.sq * a.hq);
   const int kvh = (h * a.hkv) / a.hq;
-  const float* q = (const float*)a.q + b * a.qs.b + h * a.qs.h + row * a.qs.s;
+  const float* q = (const float*)a.q + b * a.qs.b + h * a.qs.h + (size_t)row * a.qs.s;
   const float* kb = (const float*)a.k + b * a.kvs.b + kvh * a.kvs.h;
   const float* vb = (const float*)a.v + b * a.kvs.b + kvh * a.kvs.h;
-  float qv[PER], acc[PER];
+  float qr[D];   // the query row, in every lane
 #pragma unroll
-  for (int e = 0; e < PER; ++e) { qv[e] = q[lane + 64 * e]; acc[e] = 0.f; }
+  for (int d = 0; d < D; ++d) qr[d] = q[d];
+  float acc[PER];
+#pragma unroll
+  for (int e = 0; e < PER; ++e) acc[e] = 0.f;
   const int qp = a.q_pos[row];
   const int qd = a.mask == MASK_DOC_CAUSAL ? a.q_doc[row] : 0;
   const TileRange me{qp, qp, qd, qd};
@@ -59,23 +71,37 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(FwdArgs a) {
   const int nkt = n_tiles(a.sk);
   for (int t = 0; t < nkt; ++t) {
     if (!(a.flags & FLAG_NO_SKIP) && classify(me, a.kv_tiles[t], true, a.mask) == TILE_EMPTY) continue;
-    const int kend = min(a.sk, (t + 1) * TILE);
-    for (int key = t * TILE; key < kend; ++key) {
-      const int kp = a.kv_pos[key];
+    // scores: lane k takes key t*TILE + k
+    const int key = t * TILE + lane;
+    bool vis = key < a.sk;
+    float s = -INFINITY;
+    if (vis) {
       const int kd = a.mask == MASK_DOC_CAUSAL ? a.kv_doc[key] : 0;
-      if (!visible(a.mask, kp, kd, qp, qd)) continue;
-      float part = 0.f;
-#pragma unroll
-      for (int e = 0; e < PER; ++e) part += qv[e] * kb[key * a.kvs.s + lane + 64 * e];
-      const float s = wave_sum(part) * a.scale;
-      const float m_new = fmaxf(m, s);
-      const float alpha = expf(m - m_new);   // m = -inf -> 0
-      const float p = expf(s - m_new);
-      l = l * alpha + p;
-#pragma unroll
-      for (int e = 0; e < PER; ++e) acc[e] = acc[e] * alpha + p * vb[key * a.kvs.s + lane + 64 * e];
-      m = m_new;
+      vis = visible(a.mask, a.kv_pos[key], kd, qp, qd);
     }
+    if (vis) {
+      const float* kr = kb + (size_t)key * a.kvs.s;
+      float dot = 0.f;
+#pragma unroll
+      for (int d = 0; d < D; ++d) dot += qr[d] * kr[d];
+      s = dot * a.scale;
+    }
+    const float m_new = fmaxf(m, wave_max(s));
+    if (m_new == -INFINITY) continue;      // no visible key so far (uniform)
+    const float alpha = expf(m - m_new);   // m = -inf -> 0
+    const float p = vis ? expf(s - m_new) : 0.f;
+    l = l * alpha + wave_sum(p);
+#pragma unroll
+    for (int e = 0; e < PER; ++e) acc[e] *= alpha;
+    // P V: lane (+ 64 e) takes head dimension lane + 64 e; key k's probability from lane k
+    const int kn = min(TILE, a.sk - t * TILE);
+    const float* vr = vb + (size_t)t * TILE * a.kvs.s + lane;
+    for (int k = 0; k < kn; ++k) {
+      const float pk = __shfl(p, k);
+#pragma unroll
+      for (int e = 0; e < PER; ++e) acc[e] += pk * vr[(size_t)k * a.kvs.s + 64 * e];
+    }
+    m = m_new;
   }
   const float lse_t = l > 0.f ? m + logf(l) : -INFINITY;
   const float inv = l > 0.f ? 1.f / l : 0.f;
@@ -88,7 +114,7 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(FwdArgs a) {
     w_t = wt * inv;
   }
   float* op = a.o_acc + orow * D;
-  float* outp = (a.flags & FLAG_LAST) && a.out ? (float*)a.out + b * a.qs.b + h * a.qs.h + row * a.qs.s : nullptr;
+  float* outp = (a.flags & FLAG_LAST) && a.out ? (float*)a.out + b * a.qs.b + h * a.qs.h + (size_t)row * a.qs.s : nullptr;
 #pragma unroll
   for (int e = 0; e < PER; ++e) {
     float o = acc[e] * w_t;
