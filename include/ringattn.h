@@ -114,7 +114,9 @@ typedef struct {
   int32_t sq;           /* tokens of the query shard >= 0 (0 = nothing to do) */
   int32_t sk;           /* tokens of the key/value block >= 0, <= RA_MAX_SK */
   int64_t q_stride[3];  /* (batch, head, token) strides in elements of q, d_o and out */
-  int64_t kv_stride[3]; /* (batch, head, token) strides in elements of k and v */
+  int64_t kv_stride[3]; /* (batch, head, token) strides in elements of k and v; every stride a
+                           positive multiple of 8, a token stride below 2^31 / (128 x element
+                           size) (RA_ERR_UNSUPPORTED otherwise) */
   int32_t dtype;        /* ra_dtype of q, k, v, d_o and out; accumulation is fp32 */
   float softmax_scale;  /* 0 = 1/sqrt(head_dim) */
 } ra_problem;

@@ -105,6 +105,15 @@ int check_problem(const ra_problem* p) {
     if (p->kv_stride[i] <= 0 || p->kv_stride[i] % 8)
       return fail(RA_ERR_INVALID, "kv_stride[%d] = %lld must be a positive multiple of 8", i, (long long)p->kv_stride[i]);
   }
+  // The kernels stage up to 128 consecutive tokens with one 32-bit byte range (and address
+  // a token inside a staged tile with a 32-bit byte offset): 128 token strides must stay
+  // below 2^31 bytes.
+  {
+    const int64_t esize = p->dtype == RA_F32 ? 4 : 2, lim = ((int64_t)1 << 31) / (128 * esize);
+    if (p->q_stride[2] >= lim || p->kv_stride[2] >= lim)
+      return fail(RA_ERR_UNSUPPORTED, "token stride (q %lld, kv %lld elements) must be below %lld elements",
+                  (long long)p->q_stride[2], (long long)p->kv_stride[2], (long long)lim);
+  }
   if (!non_overlapping(p->q_stride, p->batch, p->hq, p->sq, p->head_dim))
     return fail(RA_ERR_INVALID, "q strides make rows overlap (out is written with them)");
   if (!std::isfinite(p->softmax_scale) || p->softmax_scale < 0.f)

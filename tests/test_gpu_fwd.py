@@ -167,6 +167,43 @@ def test_step_fwd_ragged_edges(case):
     assert max_abs(out.float().cpu().numpy(), O) <= tol_o
 
 
+def test_step_fwd_wide_token_stride():
+    """Keys 8 MiB apart (a token stride of 4 Mi elements): the K rows of the 5-tile block span more
+    than 2^31 bytes, past what one 31-bit buffer offset reaches, so each key tile is loaded
+    through a buffer resource of its own."""
+    print_case("step_fwd bf16, D=128, sk=300 keys with a token stride of 4 Mi elements")
+    rng = np.random.default_rng(77)
+    rnd = lambda *s: synthetic.bf16_round(0.5 * rng.standard_normal(s).astype(np.float32))
+    hq, sq, sk, d, stride = 2, 130, 300, 128, 4 << 20
+    assert 5 * 64 * stride * 2 >= 2 ** 31
+    q, k, v = rnd(1, hq, sq, d), rnd(1, 1, sk, d), rnd(1, 1, sk, d)
+    perm = rng.permutation(sq + sk).astype(np.int32)
+    qp, kp = perm[:sq], perm[sq:]
+
+    def wide(a):
+        n = (sk - 1) * stride + d
+        buf = torch.zeros(n, dtype=torch.bfloat16, device="cuda")
+        view = buf.as_strided((1, 1, sk, d), (n, n, stride, 1))
+        view.copy_(dev(a, torch.bfloat16))
+        return view
+    kw, vw = wide(k), wide(v)
+    o_acc = torch.zeros(1, hq, sq, d, device="cuda")
+    lse = torch.zeros(1, hq, sq, device="cuda")
+    out = torch.full((1, hq, sq, d), float("nan"), dtype=torch.bfloat16, device="cuda")
+    ra.ringattn_step_fwd(dev(q, torch.bfloat16), kw, vw, o_acc, lse, out, dev(qp, torch.int32), dev(kp, torch.int32),
+                         mask_mode=ra.RA_MASK_CAUSAL, flags=ra.RA_STEP_FIRST | ra.RA_STEP_LAST)
+    torch.cuda.synchronize()
+    O, L = oracle.attention_forward(q, k, v, qp, kp, "causal")
+    fin = np.isfinite(L)
+    got_l = lse.cpu().numpy()
+    assert np.array_equal(np.isfinite(got_l), fin)
+    assert max_abs(got_l[fin], L[fin]) <= 1e-3
+    assert max_abs(o_acc.cpu().numpy(), O) <= 1e-2
+    assert max_abs(out.float().cpu().numpy(), O) <= 1e-2
+    del kw, vw
+    torch.cuda.empty_cache()
+
+
 @pytest.mark.parametrize("d", [128, 64])
 def test_step_fwd_tile_lists_with_gaps(d):
     """Document-causal step of the last of 4 contiguous shards against its own block: the

@@ -77,6 +77,10 @@ CASES = [
     ("sk above the cap", _problem(sk=_lib.RA_MAX_SK + 1), {}, {}, _lib.RA_ERR_UNSUPPORTED),
     ("stride not a multiple of 8", _problem(q_stride=(4 * 256 * 128, 256 * 128, 132)), {}, {}, _lib.RA_ERR_INVALID),
     ("overlapping q rows", _problem(q_stride=(4 * 256 * 128, 256 * 128, 64)), {}, {}, _lib.RA_ERR_INVALID),
+    ("kv token stride of 8 Mi elements", _problem(kv_stride=(1 << 40, 1 << 35, 8 << 20)), {}, {},
+     _lib.RA_ERR_UNSUPPORTED),
+    ("q token stride of 8 Mi elements", _problem(q_stride=(1 << 40, 1 << 35, 8 << 20)), {}, {},
+     _lib.RA_ERR_UNSUPPORTED),
     ("negative scale", _problem(softmax_scale=-1.0), {}, {}, _lib.RA_ERR_INVALID),
     ("nan scale", _problem(softmax_scale=float("nan")), {}, {}, _lib.RA_ERR_INVALID),
     ("mask mode 3", _problem(), {"mask": 3}, {}, _lib.RA_ERR_UNSUPPORTED),
