@@ -285,15 +285,44 @@ def hbm_leg(steps, warmup):
     out, d_o = (torch.randn(B, H, S, D, device="cuda", generator=g).to(torch.bfloat16) for _ in range(2))
     delta = torch.empty(B, H, S, device="cuda")
 
-    res = {}
+    # the memory ceiling measured on this GPU, beside the 8 TB/s spec figure: libringattn_tools'
+    # nontemporal streaming copy and read-only sweep over 1 GiB, best over a few grid sizes
+    import ctypes
+    tools = ctypes.CDLL(os.path.join(ROOT, "ring_attention_ringattn_amd", "libringattn_tools.so"))
+    tools.ra_tool_hbm_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_void_p]
+    tools.ra_tool_hbm_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_void_p,
+                                       ctypes.c_void_p]
+    nb = 1 << 30
+    x = torch.empty(nb // 4, device="cuda").fill_(1.0)
+    y = torch.empty_like(x)
+    sink = torch.empty(8192 * 256, device="cuda")
+    st = torch.cuda.current_stream().cuda_stream
+
+    def call(rc):
+        if rc != 0:
+            raise RuntimeError(f"libringattn_tools streaming probe failed ({rc})")
+    best = {"copy": 0.0, "read": 0.0}
+    for blocks in (1024, 2048, 4096, 8192):
+        sec = event_time(lambda: call(tools.ra_tool_hbm_copy(x.data_ptr(), y.data_ptr(), nb, blocks, st)), steps, warmup)
+        best["copy"] = max(best["copy"], 2 * nb / sec / 1e9)
+        sec = event_time(lambda: call(tools.ra_tool_hbm_read(x.data_ptr(), nb, blocks, sink.data_ptr(), st)), steps,
+                         warmup)
+        best["read"] = max(best["read"], nb / sec / 1e9)
+    del x, y, sink
+    read_gbs = best["read"]
+    res = {"stream_probe": {"bytes": nb, "copy_gbs": round(best["copy"], 1), "read_gbs": round(best["read"], 1),
+                            "copy_frac_of_hbm_peak": round(best["copy"] / PEAK_HBM_GBS, 3),
+                            "read_frac_of_hbm_peak": round(best["read"] / PEAK_HBM_GBS, 3)}}
     for name, fn, per_row in (("merge", lambda: ra.ringattn_merge(o_a, l_a, o_b, l_b), 3 * (4 * D + 4)),
                               ("bwd_preprocess", lambda: ra.ringattn_bwd_preprocess(out, d_o, delta), 4 * D + 4)):
         sec = event_time(fn, steps, warmup)
         nbytes = B * H * S * per_row
         res[name] = {"us": round(sec * 1e6, 2), "algorithmic_bytes": nbytes,
-                     "gbs": round(nbytes / sec / 1e9, 1), "frac_of_hbm_peak": round(nbytes / sec / 1e9 / PEAK_HBM_GBS, 3)}
+                     "gbs": round(nbytes / sec / 1e9, 1), "frac_of_hbm_peak": round(nbytes / sec / 1e9 / PEAK_HBM_GBS, 3),
+                     "frac_of_stream_read": round(nbytes / sec / 1e9 / read_gbs, 3)}
     return {"workload": "HBM-bound kernels at the 131072-token share's shapes (16384 rows x 32 heads, D = 128): "
-                        "standalone LSE merge of two fp32 partials, backward preprocess rowsum(dO * O)",
+                        "standalone LSE merge of two fp32 partials, backward preprocess rowsum(dO * O); a measured "
+                        "streaming copy and read of 1 GiB beside them",
             **res}
 
 
