@@ -102,9 +102,11 @@ class CostModel:
 
 
 def fit_cost_model(samples: Sequence[Tuple[Sequence[int], int, float]]) -> Tuple[CostModel, float]:
-    """Least-squares fit of (alpha, beta, eps, gamma, delta) to (docs, cp, measured ms) samples,
-    weighted by 1/ms so that every sample counts by its relative error.  Returns the model
-    and the largest relative error over the samples."""
+    """Non-negative least-squares fit of (alpha, beta, eps, gamma, delta) to (docs, cp, measured ms)
+    samples, weighted by 1/ms so that every sample counts by its relative error; every term is a
+    cost, so none may come out negative.  Returns the model and the largest relative error over
+    the samples."""
+    from scipy.optimize import nnls
     rows, y = [], []
     for docs, cp, ms in samples:
         n = float(sum(docs))
@@ -112,8 +114,12 @@ def fit_cost_model(samples: Sequence[Tuple[Sequence[int], int, float]]) -> Tuple
         y.append(ms)
     a, y = np.asarray(rows), np.asarray(y)
     w = 1.0 / y
-    coef, *_ = np.linalg.lstsq(a * w[:, None], y * w, rcond=None)
-    model = CostModel(*[float(x) for x in coef])
+    # columns scaled to unit norm for the solver's conditioning (pairs ~1e9, tokens ~1e4, cp ~1)
+    aw = a * w[:, None]
+    norm = np.linalg.norm(aw, axis=0)
+    norm[norm == 0] = 1.0
+    coef, _ = nnls(aw / norm, y * w)
+    model = CostModel(*[float(x) for x in coef / norm])
     err = max(abs(model.predict(docs, cp) - ms) / ms for docs, cp, ms in samples)
     return model, err
 

@@ -71,6 +71,22 @@ def test_fit_recovers_a_known_model():
         assert getattr(fit, name) == pytest.approx(getattr(MODEL, name), rel=2e-2)
 
 
+def test_fit_keeps_every_cost_non_negative():
+    # timings with no per-token term plus noise: an unconstrained fit may trade a negative
+    # per-token cost against the others; every term is a cost, so the fit clamps it at zero
+    rng = np.random.default_rng(0)   # with this noise an unconstrained fit gives eps < 0
+    truth = dcp.CostModel(alpha=4e-8, beta=1e-4, eps=0.0, gamma=0.05, delta=0.1)
+    samples = []
+    for tot in (8192, 16384, 32768):
+        for dl in (512, 2048, 8192):
+            for c in (1, 2, 4, 8):
+                docs = [dl] * (tot // dl)
+                samples.append((docs, c, truth.predict(docs, c) * (1 + 0.05 * rng.standard_normal())))
+    fit, _ = dcp.fit_cost_model(samples)
+    assert min(fit.alpha, fit.beta, fit.eps, fit.gamma, fit.delta) >= 0.0
+    assert fit.alpha == pytest.approx(truth.alpha, rel=0.2)
+
+
 def test_cp_needed_is_the_smallest_power_of_two():
     assert [dcp.cp_needed(n, 1000, 8) for n in (1, 1000, 1001, 2000, 2001, 8000)] == [1, 1, 2, 2, 4, 8]
     with pytest.raises(ValueError):
