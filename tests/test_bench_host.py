@@ -8,6 +8,8 @@ of length L contributes L (L + 1) / 2 pairs).
 """
 import os
 import subprocess
+
+import pytest
 import sys
 
 import numpy as np
@@ -59,3 +61,26 @@ def test_packed_document_pair_count():
     total = sum(bench.visible_pairs(pos[r], pos[ra.sharding.block_of(r, t, n)], docs)
                 for r in range(n) for t in range(n))
     assert total == 271_551_562
+
+
+def test_measurement_probes_library_rejects_bad_arguments():
+    """libringattn_tools (the benchmark's matrix-core and memory probes) exports its probes and
+    rejects bad arguments on the host, before any launch."""
+    import ctypes
+    import os
+    path = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "ring_attention_ringattn_amd",
+                        "libringattn_tools.so")
+    if not os.path.exists(path):
+        pytest.skip("libringattn_tools is not built")
+    lib = ctypes.CDLL(path)
+    lib.ra_tool_mfma_peak.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    lib.ra_tool_hbm_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_void_p]
+    lib.ra_tool_hbm_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    assert lib.ra_tool_mfma_chains() == 8
+    assert lib.ra_tool_mfma_peak(0, 1, 64, None, None) == -1          # no iterations, no sink
+    assert lib.ra_tool_mfma_peak(10, 1, 96, None, None) == -1         # threads not a multiple of 64
+    assert lib.ra_tool_hbm_copy(None, None, 16, 1, None) == -1        # null buffers
+    assert lib.ra_tool_hbm_copy(16, 32, 15, 1, None) == -1            # size not a multiple of 16
+    assert lib.ra_tool_hbm_copy(16, 40, 16, 1, None) == -1            # misaligned destination
+    assert lib.ra_tool_hbm_read(16, 16, 0, 64, None) == -1            # no workgroups
+    assert lib.ra_tool_hbm_read(None, 16, 1, 64, None) == -1          # null source
