@@ -580,13 +580,23 @@ int check_run(const ra_run_desc* d) {
   return RA_OK;
 }
 
+// Flags of the events that order the copy and compute streams of a ring.  They serve
+// device-side waits only (the host never inspects them), and the kernels on either side
+// carry device-scope fences of their own in their dispatch, so the system-scope fence an event
+// performs on completion is left out: a `done` event sits between two step kernels on
+// the compute stream, where that fence (a cache write-back and invalidation) would delay
+// the next step.
+#ifndef RA_RING_EVENT_FLAGS
+#define RA_RING_EVENT_FLAGS (hipEventDisableTiming | hipEventDisableSystemFence)
+#endif
+
 struct Events {
   std::vector<hipEvent_t> ev;
   ~Events() {
     for (auto e : ev) (void)hipEventDestroy(e);
   }
   hipError_t make(hipEvent_t* out) {
-    hipError_t e = hipEventCreateWithFlags(out, hipEventDisableTiming);
+    hipError_t e = hipEventCreateWithFlags(out, RA_RING_EVENT_FLAGS);
     if (e == hipSuccess) ev.push_back(*out);
     return e;
   }

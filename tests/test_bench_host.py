@@ -84,3 +84,10 @@ def test_measurement_probes_library_rejects_bad_arguments():
     assert lib.ra_tool_hbm_copy(16, 40, 16, 1, None) == -1            # misaligned destination
     assert lib.ra_tool_hbm_read(16, 16, 0, 64, None) == -1            # no workgroups
     assert lib.ra_tool_hbm_read(None, 16, 1, 64, None) == -1          # null source
+    # timing events: null arguments are refused before any runtime call
+    lib.ra_tool_event_create.argtypes = [ctypes.c_void_p]
+    lib.ra_tool_event_elapsed_ms.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+    lib.ra_tool_event_destroy.argtypes = [ctypes.c_void_p]
+    assert lib.ra_tool_event_create(None) == -1
+    assert lib.ra_tool_event_elapsed_ms(None, None, None) == -1
+    assert lib.ra_tool_event_destroy(None) == -1
