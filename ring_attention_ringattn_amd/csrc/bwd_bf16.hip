@@ -281,7 +281,11 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a) {
   __syncthreads();
   float* xk = (float*)&QO[0][0][0];   // 4 key groups x D/32 x 16 values x 64 lanes floats
   float* xv = (float*)&KV[0][0];
-  auto slot = [&] __device__(int db, int v) { return ((kw * (D / 32) + db) * 16 + v) * 64 + lane; };
+  // the lane's id and output column again, from the lane id (not held across the loop:
+  // registers are scarce)
+  const int ln_ = __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+  const int g_ = ln_ >> 5, j_ = ln_ & 31;
+  auto slot = [&] __device__(int db, int v) { return ((kw * (D / 32) + db) * 16 + v) * 64 + ln_; };
 #pragma unroll
   for (int db = 0; db < D / 32; ++db)
 #pragma unroll
@@ -290,19 +294,30 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a) {
       else xv[slot(db, v)] = dv[db][v];
     }
   __syncthreads();
-  // C layout: lane (g, j), value v -> key kw*32 + 8*(v/4) + 4*g + v%4, dim db*32 + j
+  // C layout: lane (g, j), value v -> key kw*32 + 8*(v/4) + 4*g + v%4, dim db*32 + j.
+  // All of the lane's current values are read before any of them is written back, so the
+  // reads are in flight together (one read-modify-write at a time costs a memory round trip
+  // each).
   const size_t obase = ((size_t)b * a.hkv + kvh) * a.sk;
   float* dst = mb == 0 ? a.dk : a.dv;
   const float sc = mb == 0 ? a.scale : 1.f;
+  float old[16][D / 32];
 #pragma unroll
   for (int v = 0; v < 16; ++v) {
-    const int kr_ = k0 + kw * 32 + 8 * (v / 4) + 4 * g + (v % 4);
+    const int kr_ = k0 + kw * 32 + 8 * (v / 4) + 4 * g_ + (v % 4);
+    const float* p = dst + (obase + min(kr_, a.sk - 1)) * D;   // keys past the end reread the last key
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) old[v][db] = p[db * 32 + j_];
+  }
+#pragma unroll
+  for (int v = 0; v < 16; ++v) {
+    const int kr_ = k0 + kw * 32 + 8 * (v / 4) + 4 * g_ + (v % 4);
     if (kr_ >= a.sk) continue;
     float* p = dst + (obase + kr_) * D;
 #pragma unroll
     for (int db = 0; db < D / 32; ++db) {
       const float tot = mb == 0 ? dk[db][v] + xk[slot(db, v)] : dv[db][v] + xv[slot(db, v)];
-      p[db * 32 + j] += sc * tot;
+      p[db * 32 + j_] = old[v][db] + sc * tot;
     }
   }
 }
