@@ -488,6 +488,15 @@ __global__ __launch_bounds__(NWAVES * 64, 1) void fwd_bf16_kernel(FwdArgs a) {
   }
   float* op = a.o_acc ? a.o_acc + orow * D : nullptr;   // null: fused launch, out and lse only
   __bf16* outp = last ? (__bf16*)a.out + b * a.qs.b + h * a.qs.h + qrow * a.qs.s : nullptr;
+  // the running output is read whole before any of it is combined or written, so the reads
+  // are in flight together (a read per use would wait a memory round trip each)
+  f32x4 prev[D / 32][4];
+  if (!first) {
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int vh = 0; vh < 4; ++vh) prev[db][vh] = *(const f32x4*)(op + db * 32 + vh * 8 + g * 4);
+  }
 #pragma unroll
   for (int db = 0; db < D / 32; ++db) {
 #pragma unroll
@@ -495,7 +504,7 @@ __global__ __launch_bounds__(NWAVES * 64, 1) void fwd_bf16_kernel(FwdArgs a) {
       const int d = db * 32 + vh * 8 + g * 4;
       f32x4 o = {acc[db][vh * 4 + 0] * w_t, acc[db][vh * 4 + 1] * w_t, acc[db][vh * 4 + 2] * w_t,
                  acc[db][vh * 4 + 3] * w_t};
-      if (!first) o += w_p * *(const f32x4*)(op + d);
+      if (!first) o += w_p * prev[db][vh];
       if (op && !unchanged) *(f32x4*)(op + d) = o;
       if (last) {
         bf16x4 ob = {(__bf16)o[0], (__bf16)o[1], (__bf16)o[2], (__bf16)o[3]};
