@@ -309,3 +309,44 @@ def test_c5_full_size_packed_documents():
         print(f"  document {d} ({r.size} tokens, keys {r[0]}..{r[-1]}): dK rel L2 {ek:.3g}, dV rel L2 {ev:.3g}",
               flush=True)
         assert ek <= TOL and ev <= TOL
+
+
+def test_step_fwd_bwd_largest_block():
+    """A key/value block of RA_MAX_SK = 262144 keys (4096 tiles: the largest tile index a work-list
+    entry holds), 130 sorted query positions spread over the block (a query near the end sees every
+    tile), causal, 2/1 heads, D = 128: forward (one step, first and last) and backward, every output
+    against the oracle."""
+    sk, sq, d, hq, hkv = ra.RA_MAX_SK, 130, 128, 2, 1
+    print_case(f"step fwd+bwd bf16, sk = RA_MAX_SK = {sk}, sq = {sq}, causal, {hq}/{hkv} heads, D={d}")
+    rng = np.random.default_rng(2718)
+    rnd = lambda *s: synthetic.bf16_round(0.5 * rng.standard_normal(s).astype(np.float32))
+    q, k, v, do = rnd(1, hq, sq, d), rnd(1, hkv, sk, d), rnd(1, hkv, sk, d), rnd(1, hq, sq, d)
+    kp = np.arange(sk, dtype=np.int32)
+    edges = [0, 63, 64, sk - 65, sk - 64, sk - 1]
+    rest = rng.choice(np.setdiff1d(np.arange(sk), edges), sq - len(edges), replace=False)
+    qp = np.sort(np.concatenate([edges, rest])).astype(np.int32)
+    O, L = oracle.attention_forward(q, k, v, qp, kp, "causal", skip_masked_columns=True)
+    dQ, dK, dV = oracle.attention_backward(q, k, v, do, qp, kp, "causal", row_block=32, skip_masked_columns=True)
+    bf = torch.bfloat16
+    o_acc = torch.zeros(1, hq, sq, d, device="cuda")
+    lse = torch.zeros(1, hq, sq, device="cuda")
+    out = torch.full((1, hq, sq, d), float("nan"), dtype=bf, device="cuda")
+    qd, kd, vd = dev(q, bf), dev(k, bf), dev(v, bf)
+    qpd, kpd = dev(qp, torch.int32), dev(kp, torch.int32)
+    ra.ringattn_step_fwd(qd, kd, vd, o_acc, lse, out, qpd, kpd, None, None, mask_mode=ra.RA_MASK_CAUSAL,
+                         flags=ra.RA_STEP_FIRST | ra.RA_STEP_LAST)
+    torch.cuda.synchronize()
+    eo, el = max_abs(out.float().cpu().numpy(), O), max_abs(lse.cpu().numpy(), L)
+    print(f"  forward: O max abs {eo:.3g}, LSE max abs {el:.3g}", flush=True)
+    assert eo <= 1e-2 and el <= 1e-3
+    delta = torch.zeros(1, hq, sq, device="cuda")
+    ra.ringattn_bwd_preprocess(out, dev(do, bf), delta)
+    dq = torch.zeros(1, hq, sq, d, device="cuda")
+    dk = torch.zeros(1, hkv, sk, d, device="cuda")
+    dv = torch.zeros(1, hkv, sk, d, device="cuda")
+    ra.ringattn_step_bwd(qd, kd, vd, dev(do, bf), lse, delta, dq, dk, dv, qpd, kpd, mask_mode=ra.RA_MASK_CAUSAL)
+    torch.cuda.synchronize()
+    for got, ref, name in ((dq, dQ, "dQ"), (dk, dK, "dK"), (dv, dV, "dV")):
+        e = rel_l2(got.cpu().numpy(), ref)
+        print(f"  {name} rel L2 {e:.3g}", flush=True)
+        assert e <= TOL
