@@ -654,7 +654,8 @@ def summarize_counters(run_dirs, cal_dirs, traffic_out=None):
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=9, help="timed rings (the pages' method: 10 runs, first dropped)")
+    ap.add_argument("--steps", type=int, default=9, help="timed rings (the Dynamic-CP page's method, section "
+                    "'Resultados de benchmarks': 10 runs, first dropped)")
     ap.add_argument("--warmup", type=int, default=6,
                     help="untimed rings first: under sustained load the shader clock settles "
                          "(about 1.5 -> 1.84 GHz on MI355X) within the first ~50 ms")

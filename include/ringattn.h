@@ -1,14 +1,16 @@
 /*
  * ringattn.h -- C ABI of the per-device hot path of ring attention on MI355X.
  *
- * Ring attention (NVSHMEM-in-XLA page, section on context parallelism and
- * ring attention) splits the sequence over N ranks: every rank keeps its
+ * Ring attention (the NVSHMEM page, "Optimización en el entrenamiento de
+ * modelos de lenguaje de largo contexto con NVSHMEM en JAX y XLA", section
+ * "Paralelismo de contexto y atención en anillo") splits the sequence over N
+ * ranks: every rank keeps its
  * query shard Q_i, attends to its own key/value block and then to every other
  * rank's block as the blocks travel around a ring, computing attention
  * incrementally; the combined result equals standard attention.  The
- * Accelerate context-parallel guide (section on how it works, and its
- * pseudocode) describes the same loop as attn(Q_i, K_j, V_j) per block
- * followed by combine().  This library implements, on one GPU:
+ * Accelerate guide ("Context Parallel no 🤗 accelerate", section "Então, como
+ * funciona?" and its pseudocode) describes the same loop as attn(Q_i, K_j, V_j)
+ * per block followed by combine().  This library implements, on one GPU:
  *
  *   ringattn_step_fwd        attn(Q_i, K_j, V_j) with the combine fused in
  *   ringattn_fused_fwd       all blocks resident: attention over every block in one launch
@@ -30,8 +32,9 @@
  *   asynchronously; device faults surface at the caller's next synchronise.
  * - Validation is pure host code and runs before any HIP call.  On an error
  *   nothing is enqueued and no output is touched; ringattn_last_error() gives
- *   the reason.  Well-formed but unsupported input (the guide raises an error
- *   for attention it cannot handle: SDPA with no mask or a causal mask only)
+ *   the reason.  Well-formed but unsupported input (the Accelerate guide,
+ *   section "Como usar paralelismo de contexto?", raises an error for
+ *   attention it cannot handle: SDPA with no mask or a causal mask only)
  *   returns RA_ERR_UNSUPPORTED.
  * - Layouts.  q, d_o and out (the problem dtype) are [B][Hq][Sq][D] and k, v
  *   are [B][Hkv][Sk][D], addressed through (batch, head, token) strides in
@@ -44,8 +47,10 @@
  *   device, 0 <= pos < 2^31 - 1), shared by all batches and heads.  Documents
  *   q_doc[Sq], kv_doc[Sk] (int32, device) are needed only for
  *   RA_MASK_DOC_CAUSAL; ringattn_docs_from_cu_seqlens builds them.
- * - Mask (guide: SDPA with no mask or a causal mask; Dynamic-CP page: packed
- *   THD sequences described by cu_seqlens):
+ * - Mask (the Accelerate guide, section "Como usar paralelismo de contexto?":
+ *   SDPA with no mask or a causal mask; the Dynamic-CP page, section
+ *   "Reprogramación dinámica y empaquetado de datos": packed THD sequences
+ *   described by cu_seqlens):
  *     RA_MASK_NONE        every key visible
  *     RA_MASK_CAUSAL      key visible iff kv_pos <= q_pos
  *     RA_MASK_DOC_CAUSAL  causal and kv_doc == q_doc
@@ -130,8 +135,10 @@ size_t ringattn_step_workspace_size(const ra_problem* p);
 /*
  * One forward ring step: attention of q against one block (k_blk, v_blk),
  * merged into the running normalised result (o_acc, lse) with the exact
- * log-sum-exp combine (the pseudocode's combine, left undefined on the page,
- * read as the only combine that keeps equality with full attention).
+ * log-sum-exp combine (the combine of the Accelerate guide's pseudocode,
+ * section "Então, como funciona?", left undefined there, read as the only
+ * combine that keeps equality with full attention: the NVSHMEM page, section
+ * "Paralelismo de contexto y atención en anillo").
  *   q [B,Hq,Sq,D], k_blk/v_blk [B,Hkv,Sk,D]      (device, problem dtype, in)
  *   o_acc [B,Hq,Sq,D] fp32, lse [B,Hq,Sq] fp32    (device, in/out; out only with RA_STEP_FIRST)
  *   out [B,Hq,Sq,D] problem dtype, q_stride        (device, out, only with RA_STEP_LAST; may be NULL)
@@ -306,7 +313,9 @@ int ringattn_run(const ra_run_desc* d,
 /*
  * doc[t] = k for cu_seqlens[k] <= first_token + t < cu_seqlens[k+1], for
  * t in [0, n_tokens): the document id of each token of a packed THD stream
- * (Dynamic-CP page: cu_seqlens describes the packed sequences).  cu_seqlens
+ * (the Dynamic-CP page, "Optimización del entrenamiento variable con Dynamic
+ * Context Parallelism en Megatron Core", section "Reprogramación dinámica y
+ * empaquetado de datos": cu_seqlens describes the packed sequences).  cu_seqlens
  * [n_docs+1] int32 ascending with cu_seqlens[0] = 0 (device); doc [n_tokens]
  * int32 (device).  Tokens outside every document get doc = -1.
  */

@@ -6,17 +6,21 @@ only the tests, the smoke check and the benchmark's CPU-baseline leg do.
 What it computes (global token order, no blocking of the math):
 
 * Scores s_ij = scale * <Q_i, K_j> with scale = 1/sqrt(D) unless given (the
-  pages use SDPA, whose default scale this is: Accelerate context-parallel
-  guide, section on how to use context parallelism, the SDPA-only remark).
+  pages use SDPA, whose default scale this is: the Accelerate guide, "Context
+  Parallel no 🤗 accelerate", section "Como usar paralelismo de contexto?", the
+  SDPA-only remark).
 * Mask (same guide, same remark: no mask or a causal mask; plus the packed
-  THD layout with cu_seqlens of the Dynamic-CP page, section on dynamic
-  rescheduling and THD packing, read as "same document and causal"):
+  THD layout with cu_seqlens of the Dynamic-CP page, "Optimización del
+  entrenamiento variable con Dynamic Context Parallelism en Megatron Core",
+  section "Reprogramación dinámica y empaquetado de datos", read as "same
+  document and causal"):
     none        every pair allowed
     causal      pos_k <= pos_q   (inclusive diagonal, global positions)
     doc_causal  causal and doc_k == doc_q
 * Softmax over the allowed keys of each row, exactly as vanilla attention
-  materialises it (guide, section on why context parallelism: the full
-  score matrix of vanilla attention), LSE_i = ln sum_j exp(s_ij), and
+  materialises it (the Accelerate guide, section "Por que paralelismo de
+  contexto?": the full score matrix of vanilla attention), LSE_i = ln sum_j
+  exp(s_ij), and
   O_i = sum_j P_ij V_j.  A row with no allowed key has LSE = -inf, O = 0.
 * GQA: q-head h reads kv-head floor(h * Hkv / Hq).
 * Backward of L = sum(O * dO): D_i = <dO_i, O_i>, dP_ij = <dO_i, V_j>,

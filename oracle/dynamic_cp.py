@@ -1,7 +1,9 @@
 """Exhaustive Dynamic-CP planner: the optimum the product's heuristic solver is checked against.
 
 TEST INFRASTRUCTURE (see the package header).  The problem is the one the
-Dynamic-CP page (Megatron Core) gives its solver: pack variable-length
+Dynamic-CP page ("Optimización del entrenamiento variable con Dynamic Context
+Parallelism en Megatron Core", section "Modelado del programador de datos") gives
+its solver: pack variable-length
 sequences into micro-batches and choose a context-parallel size per
 micro-batch so as to maximise efficiency without exceeding the GPU memory
 limit.  Written out (the same readings the product documents):

@@ -6,15 +6,18 @@ This is the method written in the pages' order, used only to check the
 method itself against the plain definition in ``attention.py``:
 
 * Sequence sharding: a tensor sharded along a dimension over N ranks is cut
-  into N equal parts (Accelerate context-parallel guide, technical details,
-  definition of a shard).  The zigzag variant cuts 2N equal chunks and gives
+  into N equal parts (the Accelerate guide, "Context Parallel no 🤗 accelerate",
+  section "Detalhes técnicos", the definition of a shard).  The zigzag variant
+  cuts 2N equal chunks and gives
   rank r chunks r and 2N-1-r; it is not on the pages and is the usual
   load-balanced reading for causal masks.
 * Each rank keeps its Q shard, attends first to its own K/V block, then to
   every other rank's block once, each block arriving from the previous rank
-  of the ring (same guide, "how does it work" and the ring-rotation
-  paragraph; NVSHMEM/XLA page, ring attention section: send KV to the next
-  device, compute incrementally while blocks circulate).  At step t rank r
+  of the ring (same guide, section "Então, como funciona?" and its
+  ring-rotation paragraph; the NVSHMEM page, "Optimización en el entrenamiento
+  de modelos de lenguaje de largo contexto con NVSHMEM en JAX y XLA", section
+  "Paralelismo de contexto y atención en anillo": send KV to the next device,
+  compute incrementally while blocks circulate).  At step t rank r
   holds block (r - t) mod N.
 * The per-block partial results are combined; the pages leave ``combine``
   undefined.  The reading taken: the exact log-sum-exp merge of normalised

@@ -1,7 +1,9 @@
 """Dynamic context parallelism: an attention cost model and a packing / CP-size solver.
 
-Follows the Dynamic-CP page (Megatron Core), section on modelling the data
-scheduler: a cost model estimates each sample's run time from its sequence
+Follows the Dynamic-CP page ("Optimización del entrenamiento variable con Dynamic
+Context Parallelism en Megatron Core"), sections "Modelado del programador de
+datos" and "Colaboración del modelo de costos, solucionador y simulador": a cost
+model estimates each sample's run time from its sequence
 length (attention work grows with the square of the length), and a solver
 uses it to pack variable-length sequences into micro-batches and to choose a
 context-parallel size per micro-batch, maximising efficiency without
@@ -33,7 +35,8 @@ The page gives no formulas; the readings taken here:
   part in; the iteration takes as long as the most loaded GPU (data-parallel
   ranks wait for each other at the gradient synchronisation, the imbalance
   the page describes).
-* Baseline ("packing only", the page's Table 1 reference): one static CP size,
+* Baseline ("packing only", the reference of the page's Table 1, section
+  "Resultados de benchmarks"): one static CP size,
   set by the longest sequence, for every micro-batch; sequences packed to the
   same token budget.
 

@@ -1,8 +1,9 @@
 """Sequence sharding of a ring: which global tokens each rank holds.
 
 Host-side bookkeeping (no attention math).  A tensor sharded along the
-sequence over N ranks is cut into N equal parts (Accelerate context-parallel
-guide, technical details, definition of a shard): ``contiguous`` gives rank r
+sequence over N ranks is cut into N equal parts (the Accelerate guide, "Context
+Parallel no 🤗 accelerate", section "Detalhes técnicos", the definition of a
+shard): ``contiguous`` gives rank r
 tokens [r S/N, (r+1) S/N).  ``zigzag`` cuts 2N chunks of c = S/2N tokens and
 gives rank r chunk r followed by chunk 2N-1-r, which balances a causal mask:
 every rank then has the same number of visible (query, key) pairs at every
@@ -84,8 +85,8 @@ def unshard_buffers(shards, seq_dim: int, scheme: str = "zigzag"):
 
 def shift_labels(labels, seq_dim: int = 1, ignore_index: int = -100):
     """Causal-LM targets: token t's label is token t+1, the last position gets
-    `ignore_index`.  Shift BEFORE sharding (Accelerate context-parallel guide, on
-    labels that are a copy of the input ids): a shard cannot see the first token of
+    `ignore_index`.  Shift BEFORE sharding (the Accelerate guide, section "Interface
+    do Accelerate", on labels that are a copy of the input ids): a shard cannot see the first token of
     the next shard, so shifting after sharding misaligns every shard's last label."""
     try:
         import torch
@@ -106,7 +107,8 @@ def shift_labels(labels, seq_dim: int = 1, ignore_index: int = -100):
 
 class maybe_context_parallel:
     """Context manager that shards torch buffers in place along their sequence
-    dimension for the block (Accelerate context-parallel guide: the
+    dimension for the block (the Accelerate guide, sections "Como usar paralelismo de
+    contexto?" and "Interface do Accelerate": the
     `maybe_context_parallel(buffers, buffer_seq_dims, no_restore_buffers)` pattern).
 
     It is a no-op when context parallelism is off (`n` is None or 1).  Otherwise,

@@ -12,7 +12,8 @@ disagrees with:
   in float64 on the CPU, SciPy's logsumexp),
 * a 50-digit Decimal brute force on tiny inputs,
 * central finite differences of the forward,
-* the memory arithmetic the Accelerate guide prints.
+* the memory arithmetic the Accelerate guide prints ("Context Parallel no 🤗
+  accelerate", section "Por que paralelismo de contexto?").
 """
 from __future__ import annotations
 

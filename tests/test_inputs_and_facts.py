@@ -14,7 +14,8 @@ def test_attention_matrix_memory_fact():
     s = g["seq_len"]
     assert s * s * g["bytes_per_element_bf16"] == g["bytes_per_head"] == 2 ** 35
     assert g["bytes_per_head"] / 2 ** 30 == g["gib_per_head"]
-    # the guide's "~32 GB" also holds for the decimal reading 128000
+    # the Accelerate guide's "~32 GB" (section "Por que paralelismo de contexto?") also holds
+    # for the decimal reading 128000
     assert abs(128000 ** 2 * 2 / 1e9 - 32.768) < 1e-9
 
 
