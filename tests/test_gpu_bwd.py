@@ -53,6 +53,15 @@ def test_bwd_zigzag_ring_all_ranks():
     ring = Ring(inp["q"], inp["k"], inp["v"], pos, "causal", "bf16", range(4), do_glob=inp["do"])
     ring.forward().backward()
     _check(ring, inp, "causal")
+    # the other staging modes give the same bits: serial copies, DMA-engine copies, poisoned slots
+    ref = [[t.clone() for t in getattr(ring, n)] for n in ("dq", "dk", "dv")]
+    for flags, cs in ((ra.RA_RUN_SERIAL_COPY, "side"), (ra.RA_RUN_COPY_ENGINE, "side"),
+                      (ra.RA_RUN_COPY_ENGINE | ra.RA_RUN_POISON, "side"), (ra.RA_RUN_POISON, "side")):
+        print(f"  backward flags {flags}", flush=True)
+        ring.backward(flags=flags, copy_stream=cs)
+        for n, r in zip(("dq", "dk", "dv"), ref):
+            for x, y in zip(getattr(ring, n), r):
+                assert torch.equal(x, y), (flags, n)
 
 
 def test_bwd_rank_share_medium():

@@ -263,12 +263,14 @@ def _small_zigzag_ring(n=4, seq=2048, seed=7, mask="causal", ranks=None):
 
 
 def test_run_modes_are_bitwise_equal():
-    """Overlapped prefetch, serial copies, poisoned slots and no tile skipping give identical bits."""
-    print_case("run modes: overlapped vs serial vs poison vs no-skip, 8-rank zigzag, all ranks")
+    """Overlapped prefetch, serial copies, DMA-engine copies, poisoned slots and no tile skipping
+    give identical bits."""
+    print_case("run modes: overlapped vs serial vs DMA engine vs poison vs no-skip, 8-rank zigzag, all ranks")
     ring, _, _ = _small_zigzag_ring(n=8, seq=4096)
     ring.forward()
     ref = [t.clone() for t in ring.o_acc], [t.clone() for t in ring.lse], [t.clone() for t in ring.out]
     for flags, cs in ((ra.RA_RUN_SERIAL_COPY, "side"), (0, None), (ra.RA_RUN_POISON, "side"),
+                      (ra.RA_RUN_COPY_ENGINE, "side"), (ra.RA_RUN_COPY_ENGINE | ra.RA_RUN_POISON, "side"),
                       (ra.RA_NO_SKIP, "side")):
         print(f"  flags {flags} copy stream {cs}", flush=True)
         ring.forward(flags=flags, copy_stream=cs)
