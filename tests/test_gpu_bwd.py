@@ -359,3 +359,60 @@ def test_step_fwd_bwd_largest_block():
         e = rel_l2(got.cpu().numpy(), ref)
         print(f"  {name} rel L2 {e:.3g}", flush=True)
         assert e <= TOL
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_step_fwd_bwd_explicit_scale_and_no_skip(dtype):
+    """A softmax scale other than 1/sqrt(D) (0.3), forward and backward against the oracle at that
+    scale; the backward again with tile skipping off gives the same bits (fully masked tiles add
+    exact zeros)."""
+    d, B, hq, hkv, sq, sk, scale = 128, 1, 4, 2, 190, 333, 0.3
+    print_case(f"step fwd+bwd {dtype}, softmax_scale {scale}, causal, D={d}, sq={sq}, sk={sk}; bwd with RA_NO_SKIP")
+    rng = np.random.default_rng(31415)
+    wdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    rnd = (lambda *s: synthetic.bf16_round(0.5 * rng.standard_normal(s).astype(np.float32))) if dtype == "bf16" \
+        else (lambda *s: rng.standard_normal(s).astype(np.float32))
+    q, k, v, do = rnd(B, hq, sq, d), rnd(B, hkv, sk, d), rnd(B, hkv, sk, d), rnd(B, hq, sq, d)
+    perm = rng.permutation(sq + sk).astype(np.int32)
+    qp, kp = np.maximum(perm[:sq], 5).astype(np.int32), perm[sq:]
+    kp[0] = 0
+    O, L = oracle.attention_forward(q, k, v, qp, kp, "causal", scale=scale)
+    dQ, dK, dV = oracle.attention_backward(q, k, v, do, qp, kp, "causal", scale=scale)
+    o_acc = torch.zeros(B, hq, sq, d, device="cuda")
+    lse = torch.zeros(B, hq, sq, device="cuda")
+    out = torch.full((B, hq, sq, d), float("nan"), dtype=wdt, device="cuda")
+    qd, kd, vd, dod = dev(q, wdt), dev(k, wdt), dev(v, wdt), dev(do, wdt)
+    qpd, kpd = dev(qp, torch.int32), dev(kp, torch.int32)
+    ra.ringattn_step_fwd(qd, kd, vd, o_acc, lse, out, qpd, kpd, mask_mode=ra.RA_MASK_CAUSAL,
+                         flags=ra.RA_STEP_FIRST | ra.RA_STEP_LAST, softmax_scale=scale)
+    torch.cuda.synchronize()
+    tol_o, tol_l = (1e-2, 1e-3) if dtype == "bf16" else (1e-5, 1e-5)
+    eo, el = max_abs(out.float().cpu().numpy(), O), max_abs(lse.cpu().numpy(), L)
+    print(f"  forward: O max abs {eo:.3g}, LSE max abs {el:.3g}", flush=True)
+    assert eo <= tol_o and el <= tol_l
+    # the backward from the oracle's O and LSE (as the other step tests), so it is checked on its own
+    delta = torch.zeros(B, hq, sq, device="cuda")
+    ra.ringattn_bwd_preprocess(dev(O, wdt), dod, delta)
+    lse_ref = dev(L)
+    grads = []
+    for flags in (0, ra.RA_NO_SKIP):
+        dq = torch.zeros(B, hq, sq, d, device="cuda")
+        dk = torch.zeros(B, hkv, sk, d, device="cuda")
+        dv = torch.zeros(B, hkv, sk, d, device="cuda")
+        ra.ringattn_step_bwd(qd, kd, vd, dod, lse_ref, delta, dq, dk, dv, qpd, kpd, mask_mode=ra.RA_MASK_CAUSAL,
+                             flags=flags, softmax_scale=scale)
+        torch.cuda.synchronize()
+        grads.append((dq, dk, dv))
+    for got, ref, name in zip(grads[0], (dQ, dK, dV), ("dQ", "dK", "dV")):
+        if dtype == "bf16":
+            e = rel_l2(got.cpu().numpy(), ref)
+            print(f"  {name} rel L2 {e:.3g}", flush=True)
+            assert e <= TOL
+        else:
+            # the fp32 bound of 1e-5 is for values of order one; at this scale the gradients reach
+            # about 12 and fp32 rounding grows with them, so the bound scales with the largest value
+            e, m = max_abs(got.cpu().numpy(), ref), float(np.max(np.abs(ref)))
+            print(f"  {name} max abs {e:.3g} (largest |value| {m:.3g})", flush=True)
+            assert e <= 1e-5 * max(1.0, m)
+    for x, y in zip(grads[0], grads[1]):
+        assert torch.equal(x, y)
