@@ -640,6 +640,14 @@ def summarize_counters(run_dirs, cal_dirs, traffic_out=None):
         json.dump({"kernel": kgb[0], "grid_threads": kgb[1],
                    "workload": "131072-token rank share, one ring step (16384 queries x 16384 keys, 32/8 heads, "
                                "D = 128): every launch of the headline ring",
+                   "commands": [f"rocprofv3 --pmc {c} --output-format csv -d gpurun_out/pmc_c3_{n} -o run -- "
+                                "python3 bench.py --legs \"\" --no-cpu-baseline --steps 1 --warmup 1"
+                                for c, n in (("FETCH_SIZE", "fetch"), ("WRITE_SIZE", "write"))]
+                               + [f"rocprofv3 --pmc {c} --output-format csv -d gpurun_out/pmc_cal_{n} -o run -- "
+                                  "python3 bench.py --copy-calibration"
+                                  for c, n in (("FETCH_SIZE", "fetch"), ("WRITE_SIZE", "write"))]
+                               + ["python3 bench.py --summarize-counters " + " ".join(run_dirs) + " --calibration "
+                                  + " ".join(cal_dirs) + " --traffic-out " + traffic_out],
                    "kernel_source_sha256": kernel_source_hash(),
                    "copy_calibration": {"bytes_read_and_written_per_copy": copy_bytes, "fetch_kib_raw": fetch_kib,
                                         "write_kib_raw": write_kib, "fetch_scale": fscale, "write_scale": wscale},
