@@ -407,13 +407,25 @@ def _cpu_worker_init():
 
 
 def _cpu_task(task):
-    """The oracle forward of a few query rows of one head against every visible key."""
+    """The oracle forward (or forward and backward) of a few query rows of one head against every
+    visible key; returns the visible (row, key) pairs."""
     import numpy as np
 
     import oracle
     wname, h, rows = task
-    w, pos_rows, inp = _CPU[wname]
+    w, pos_rows, inp = _CPU[wname][:3]
     kvh = h * w.hkv // w.hq
+    if wname in ("c4", "c5"):   # GQA group 0 only: query heads 0-3 and kv head 0 were drawn
+        doc = _CPU[wname][3]
+        mode = "doc_causal" if doc is not None else "causal"
+        qd = None if doc is None else doc[pos_rows[rows]]
+        oracle.attention_backward(inp["q"][:, h:h + 1, rows], inp["k"], inp["v"], inp["do"][:, h:h + 1, rows],
+                                  pos_rows[rows], np.arange(w.seq), mode, qd, doc, row_block=128,
+                                  skip_masked_columns=True)
+        if doc is None:
+            return int((pos_rows[rows] + 1).sum())
+        starts = np.concatenate([[0], np.cumsum(np.bincount(doc))])
+        return int((pos_rows[rows] - starts[doc[pos_rows[rows]]] + 1).sum())
     oracle.attention_forward(inp["q"][:, h:h + 1, rows], inp["k"][:, kvh:kvh + 1], inp["v"][:, kvh:kvh + 1],
                              pos_rows[rows], np.arange(w.seq), "causal", row_block=128,
                              skip_masked_columns=True)
@@ -444,7 +456,10 @@ def cpu_baseline(c3_host, budget_s):
     processes over (head, 8 query rows) tasks.  Headline: a bounded sample of the 131072-token
     share (per head 64 seeded random rows plus the zigzag chunk edges, all visible keys), for at
     most `budget_s` seconds of wall time; beside it the 512-token fp32 ring and the 8192-token
-    ring in full.  Runs before the GPU is touched (forking then is safe)."""
+    ring in full, and forward + backward of bounded samples of the 262144-token share and of the
+    packed documents (GQA group 0: query heads 0-3 against kv head 0, per head 64 seeded random
+    rows; at most budget_s / 3 seconds each).  Runs before the GPU is touched (forking then is
+    safe)."""
     import multiprocessing
 
     import numpy as np
@@ -461,6 +476,22 @@ def cpu_baseline(c3_host, budget_s):
         small[name] = w
     workers = max(1, min(16, len(os.sched_getaffinity(0))))
     rng = np.random.default_rng(0)
+    # GQA group 0 of the 262144-token share (rank 0's rows) and of the packed documents (all rows)
+    import ring_attention_ringattn_amd as ra
+    group_rows = {}
+    for name in ("c4", "c5"):
+        w = synthetic.WORKLOADS[name]
+        cand = ra.sharding.shard_positions(w.seq, w.n_shards, w.sharding)[0] if name == "c4" else np.arange(w.seq)
+        rows = np.sort(rng.choice(cand, 64, replace=False))
+        gq = w.hq // w.hkv
+        inp = {"q": synthetic.draw_rows(w, synthetic.TAG_Q, gq, rows, w.value_scale),
+               "do": synthetic.draw_rows(w, synthetic.TAG_DO, gq, rows, w.do_scale),
+               "k": synthetic.draw_rows(w, synthetic.TAG_K, 1, np.arange(w.seq), w.value_scale),
+               "v": synthetic.draw_rows(w, synthetic.TAG_V, 1, np.arange(w.seq), w.value_scale)}
+        cu = synthetic.cu_seqlens(w)
+        doc = None if cu is None else (np.searchsorted(cu, np.arange(w.seq), side="right") - 1).astype(np.int32)
+        _CPU[name] = (w, rows, inp, doc)
+        group_rows[name] = gq
     c = wc.seq // (2 * wc.n_shards)
     n_local = rows_pos.size
     tasks = {}
@@ -470,22 +501,28 @@ def cpu_baseline(c3_host, budget_s):
     for name, w in small.items():
         n = _CPU[name][1].size
         tasks[name] = [(name, h, np.arange(i, min(n, i + 64))) for i in range(0, n, 64) for h in range(w.hq)]
+    for name, gq in group_rows.items():
+        tasks[name] = [(name, h, np.arange(i, i + 8)) for i in range(0, 64, 8) for h in range(gq)]
     model, npver, blas = _host_facts()
     ctx = multiprocessing.get_context("fork")
     res = {}
-    with ctx.Pool(workers, initializer=_cpu_worker_init) as pool:
-        for name in ("c3", "c1", "c2"):
-            w = _CPU[name][0]
+    for name in ("c3", "c1", "c2", "c4", "c5"):
+        w = _CPU[name][0]
+        limit = budget_s if name == "c3" else budget_s / 3 if name in ("c4", "c5") else None
+        flop_per_pair = 14.0 if name in ("c4", "c5") else 4.0   # forward + backward: 4 + 10 per D
+        # a pool per workload, ended when its budget is spent, so that no task of one workload
+        # still runs while the next one is timed
+        with ctx.Pool(workers, initializer=_cpu_worker_init) as pool:
             done = pairs = 0
             t0 = time.perf_counter()
             for p in pool.imap_unordered(_cpu_task, tasks[name]):
                 pairs += p
                 done += 1
-                if name == "c3" and time.perf_counter() - t0 > budget_s:
+                if limit is not None and time.perf_counter() - t0 > limit:
                     break
             sec = time.perf_counter() - t0
-            res[name] = (done, len(tasks[name]), pairs, sec, 4.0 * w.head_dim * pairs / sec / 1e12)
-        pool.terminate()
+            pool.terminate()
+        res[name] = (done, len(tasks[name]), pairs, sec, flop_per_pair * w.head_dim * pairs / sec / 1e12)
     done, total, pairs, sec, tf = res["c3"]
     return {"value": round(tf, 5), "unit": "TFLOP/s", "cores": workers, "kind": "oracle",
             "sample": f"fp64 oracle forward (numpy) of {done} of {total} tasks of the 131072-token rank share: "
@@ -498,7 +535,12 @@ def cpu_baseline(c3_host, budget_s):
                        "tflops": round(res[name][4], 5)}
                 for name, label in (("c1", "fp32 512-token ring, full forward of all 4 ranks (2 heads, D = 64)"),
                                     ("c2", "8192-token zigzag ring, full forward of all 4 ranks (32/8 heads, "
-                                           "D = 128)"))}}
+                                           "D = 128)"),
+                                    ("c4", "262144-token share, forward + backward (dQ and the rows' dK, dV "
+                                           "contributions) of GQA group 0 (query heads 0-3, kv head 0) on 64 "
+                                           "seeded random rows of rank 0, all visible keys"),
+                                    ("c5", "packed documents, forward + backward of GQA group 0 on 64 seeded "
+                                           "random rows of the 65536 tokens, document-causal"))}}
 
 
 # ------------------------------------------------------------------ trace summaries (profiles/)
