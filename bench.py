@@ -399,6 +399,8 @@ def mfma_peak_leg(steps, warmup):
 # ------------------------------------------------------------------ CPU baseline (fp64 oracle)
 
 _CPU = {}   # host inputs the forked workers read (set before the pool starts)
+CPU_C3_ROWS = 384                        # seeded random rows per query head of the headline sample
+CPU_GROUP_ROWS = {"c4": 256, "c5": 512}  # seeded random rows of the forward+backward samples
 
 
 def _cpu_worker_init():
@@ -454,11 +456,11 @@ def _host_facts():
 def cpu_baseline(c3_host, budget_s):
     """The fp64 oracle, as it stands, on the host's cores: a fork pool of one-BLAS-thread
     processes over (head, 8 query rows) tasks.  Headline: a bounded sample of the 131072-token
-    share (per head 64 seeded random rows plus the zigzag chunk edges, all visible keys), for at
+    share (per head CPU_C3_ROWS seeded random rows plus the zigzag chunk edges, all visible keys), for at
     most `budget_s` seconds of wall time; beside it the 512-token fp32 ring and the 8192-token
     ring in full, and forward + backward of bounded samples of the 262144-token share and of the
-    packed documents (GQA group 0: query heads 0-3 against kv head 0, per head 64 seeded random
-    rows; at most budget_s / 3 seconds each).  Runs before the GPU is touched (forking then is
+    packed documents (GQA group 0: query heads 0-3 against kv head 0, per head CPU_GROUP_ROWS seeded
+    random rows; at most budget_s / 3 seconds each).  Runs before the GPU is touched (forking then is
     safe)."""
     import multiprocessing
 
@@ -482,7 +484,7 @@ def cpu_baseline(c3_host, budget_s):
     for name in ("c4", "c5"):
         w = synthetic.WORKLOADS[name]
         cand = ra.sharding.shard_positions(w.seq, w.n_shards, w.sharding)[0] if name == "c4" else np.arange(w.seq)
-        rows = np.sort(rng.choice(cand, 64, replace=False))
+        rows = np.sort(rng.choice(cand, CPU_GROUP_ROWS[name], replace=False))
         gq = w.hq // w.hkv
         inp = {"q": synthetic.draw_rows(w, synthetic.TAG_Q, gq, rows, w.value_scale),
                "do": synthetic.draw_rows(w, synthetic.TAG_DO, gq, rows, w.do_scale),
@@ -496,13 +498,14 @@ def cpu_baseline(c3_host, budget_s):
     n_local = rows_pos.size
     tasks = {}
     for h in range(wc.hq):
-        rows = np.unique(np.concatenate([rng.choice(n_local, 64, replace=False), [0, c - 1, c, 2 * c - 1]]))
+        rows = np.unique(np.concatenate([rng.choice(n_local, CPU_C3_ROWS, replace=False), [0, c - 1, c, 2 * c - 1]]))
         tasks.setdefault("c3", []).extend(("c3", h, rows[i:i + 8]) for i in range(0, rows.size, 8))
     for name, w in small.items():
         n = _CPU[name][1].size
         tasks[name] = [(name, h, np.arange(i, min(n, i + 64))) for i in range(0, n, 64) for h in range(w.hq)]
     for name, gq in group_rows.items():
-        tasks[name] = [(name, h, np.arange(i, i + 8)) for i in range(0, 64, 8) for h in range(gq)]
+        n_rows = CPU_GROUP_ROWS[name]
+        tasks[name] = [(name, h, np.arange(i, i + 8)) for i in range(0, n_rows, 8) for h in range(gq)]
     model, npver, blas = _host_facts()
     ctx = multiprocessing.get_context("fork")
     res = {}
@@ -526,7 +529,7 @@ def cpu_baseline(c3_host, budget_s):
     done, total, pairs, sec, tf = res["c3"]
     return {"value": round(tf, 5), "unit": "TFLOP/s", "cores": workers, "kind": "oracle",
             "sample": f"fp64 oracle forward (numpy) of {done} of {total} tasks of the 131072-token rank share: "
-                      f"per head 64 seeded random query rows plus the zigzag chunk edges, 8 rows x 1 head per "
+                      f"per head {CPU_C3_ROWS} seeded random query rows plus the zigzag chunk edges, 8 rows x 1 head per "
                       f"task, all visible keys; {pairs} visible (row, key) pairs over the sampled heads in "
                       f"{sec:.1f} s wall; a fork pool of {workers} processes with one BLAS thread each; "
                       f"host CPU {model}; numpy {npver}; BLAS {blas}",
@@ -537,10 +540,11 @@ def cpu_baseline(c3_host, budget_s):
                                     ("c2", "8192-token zigzag ring, full forward of all 4 ranks (32/8 heads, "
                                            "D = 128)"),
                                     ("c4", "262144-token share, forward + backward (dQ and the rows' dK, dV "
-                                           "contributions) of GQA group 0 (query heads 0-3, kv head 0) on 64 "
-                                           "seeded random rows of rank 0, all visible keys"),
-                                    ("c5", "packed documents, forward + backward of GQA group 0 on 64 seeded "
-                                           "random rows of the 65536 tokens, document-causal"))}}
+                                           "contributions) of GQA group 0 (query heads 0-3, kv head 0) on "
+                                           f"{CPU_GROUP_ROWS['c4']} seeded random rows of rank 0, all visible keys"),
+                                    ("c5", f"packed documents, forward + backward of GQA group 0 on "
+                                           f"{CPU_GROUP_ROWS['c5']} seeded random rows of the 65536 tokens, "
+                                           "document-causal"))}}
 
 
 # ------------------------------------------------------------------ trace summaries (profiles/)
@@ -775,6 +779,9 @@ def main():
         torch.cuda.synchronize()
         t_ring = (time.perf_counter() - t0) / args.steps
     kern_ms = [sum(ev.elapsed_ms(hs[2 * t], hs[2 * t + 1]) for hs in handles) / args.steps for t in range(n)]
+    # each timed ring from its first step's start to its last step's end (the tile tables and step
+    # 0's value transpose before the first step are outside this span, inside ms_per_step)
+    spans = sorted(ev.elapsed_ms(hs[0], hs[2 * n - 1]) for hs in handles)
     ev.close()
     achieved = flops_ring / (sum(kern_ms) / 1e3) / 1e12
 
@@ -800,6 +807,8 @@ def main():
         # ring time not covered by the step kernels: launch gaps between steps, the tile tables, the
         # transpose of step 0's home value block on the compute stream, and any wait for a staging copy
         "exposed_ms_per_ring": round(t_ring * 1e3 - sum(kern_ms), 4),
+        "ring_span_ms": {"min": round(spans[0], 4), "median": round(spans[len(spans) // 2], 4),
+                         "mean": round(sum(spans) / len(spans), 4), "max": round(spans[-1], 4)},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": measured_traffic(),
                      "kernel": "ra::fwd_bf16_kernel<128,*>",
