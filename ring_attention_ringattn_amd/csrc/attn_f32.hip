@@ -71,6 +71,18 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(FwdArgs a) {
   const int nkt = n_tiles(a.sk);
   for (int t = 0; t < nkt; ++t) {
     if (!(a.flags & FLAG_NO_SKIP) && classify(me, a.kv_tiles[t], true, a.mask) == TILE_EMPTY) continue;
+    // A whole tile's V rows (lane (+ 64 e): head dimension lane + 64 e) are loaded here,
+    // together with the K rows of the scores: they do not depend on the scores, and loads
+    // issued together take one memory round trip instead of one each.
+    const int kn = min(TILE, a.sk - t * TILE);
+    const float* vr = vb + (size_t)t * TILE * a.kvs.s + lane;
+    float vt[TILE][PER];
+    if (kn == TILE) {
+#pragma unroll
+      for (int k = 0; k < TILE; ++k)
+#pragma unroll
+        for (int e = 0; e < PER; ++e) vt[k][e] = vr[(size_t)k * a.kvs.s + 64 * e];
+    }
     // scores: lane k takes key t*TILE + k
     const int key = t * TILE + lane;
     bool vis = key < a.sk;
@@ -94,12 +106,20 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(FwdArgs a) {
 #pragma unroll
     for (int e = 0; e < PER; ++e) acc[e] *= alpha;
     // P V: lane (+ 64 e) takes head dimension lane + 64 e; key k's probability from lane k
-    const int kn = min(TILE, a.sk - t * TILE);
-    const float* vr = vb + (size_t)t * TILE * a.kvs.s + lane;
-    for (int k = 0; k < kn; ++k) {
-      const float pk = __shfl(p, k);
+    // (a whole tile from the rows loaded above; a partial one with a plain loop)
+    if (kn == TILE) {
 #pragma unroll
-      for (int e = 0; e < PER; ++e) acc[e] += pk * vr[(size_t)k * a.kvs.s + 64 * e];
+      for (int k = 0; k < TILE; ++k) {
+        const float pk = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(p), k));
+#pragma unroll
+        for (int e = 0; e < PER; ++e) acc[e] += pk * vt[k][e];
+      }
+    } else {
+      for (int k = 0; k < kn; ++k) {
+        const float pk = __shfl(p, k);
+#pragma unroll
+        for (int e = 0; e < PER; ++e) acc[e] += pk * vr[(size_t)k * a.kvs.s + 64 * e];
+      }
     }
     m = m_new;
   }
