@@ -43,7 +43,8 @@ PEAK_HBM_GBS = 8000.0
 N_CU, BF16_FLOP_PER_CLK_CU = 256, 4096
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fwd_bf16_c3_traffic.json")
 KERNEL_SOURCES = ("ring_attention_ringattn_amd/csrc/fwd_bf16.hip", "ring_attention_ringattn_amd/csrc/mfma_tile.h",
-                  "ring_attention_ringattn_amd/csrc/ra_internal.h")
+                  "ring_attention_ringattn_amd/csrc/ra_internal.h",
+                  "ring_attention_ringattn_amd/build.py")   # its compiler options shape the kernel too
 METRIC = "causal-effective attention TFLOP/s per rank-share (fwd, fwd+bwd); % bf16 MFMA peak"
 ALL_LEGS = ("allgather", "hbm", "mfma_peak", "c1", "c2", "c4", "c5")
 
