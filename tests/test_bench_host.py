@@ -91,3 +91,44 @@ def test_measurement_probes_library_rejects_bad_arguments():
     assert lib.ra_tool_event_create(None) == -1
     assert lib.ra_tool_event_elapsed_ms(None, None, None) == -1
     assert lib.ra_tool_event_destroy(None) == -1
+
+
+def test_traffic_counters_are_reported_only_for_the_sources_they_were_taken_on(tmp_path, monkeypatch):
+    """roofline.traffic comes from the committed counter summary only while the forward
+    kernel's sources (and the build options in build.py) hash to the value recorded with it."""
+    import json
+    src = tmp_path / "kernel.hip"
+    src.write_text("// one version of the kernel\n")
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    monkeypatch.setattr(bench, "KERNEL_SOURCES", ("kernel.hip",))
+    summary = tmp_path / "traffic.json"
+    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(summary))
+    assert bench.measured_traffic() is None   # no summary
+    summary.write_text(json.dumps({"kernel_source_sha256": bench.kernel_source_hash(), "hbm_bytes_per_launch": 123.0}))
+    assert bench.measured_traffic() == 123.0
+    src.write_text("// the kernel changed after the counters were taken\n")
+    assert bench.measured_traffic() is None
+
+
+def test_forward_build_options_are_part_of_the_counter_hash():
+    assert "ring_attention_ringattn_amd/build.py" in bench.KERNEL_SOURCES
+    assert "ring_attention_ringattn_amd/csrc/fwd_bf16.hip" in bench.KERNEL_SOURCES
+
+
+def test_per_source_compiler_options_reach_only_their_file(monkeypatch, tmp_path):
+    from ring_attention_ringattn_amd import build as B
+    seen = {}
+
+    class Done:
+        returncode, stderr = 0, ""
+
+    def fake_run(cmd, capture_output, text):
+        seen[os.path.basename(cmd[cmd.index("-c") + 1])] = cmd
+        return Done()
+    monkeypatch.setattr(B.subprocess, "run", fake_run)
+    for name in ("fwd_bf16.hip", "bwd_bf16.hip"):
+        B._compile(os.path.join(B.CSRC, name), (), str(tmp_path))
+    assert "--amdgpu-sched-strategy=iterative-ilp" in seen["fwd_bf16.hip"]
+    assert not any("sched-strategy" in c for c in seen["bwd_bf16.hip"])
+    for cmd in seen.values():   # packed fp32 arithmetic stays off everywhere
+        assert "-packed-fp32-ops" in cmd
